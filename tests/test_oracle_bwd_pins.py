@@ -1,0 +1,68 @@
+"""Pins of the fp64 backward oracle: central finite differences of the
+decision-frozen forward, and torch autograd of library attention."""
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as orc
+
+
+def _loss(Q, K, V, dO, L_src, L_ctx, b, sel, flat):
+    O, _ = orc.isa_ref_fixed(Q, K, V, L_src, L_ctx, b, sel, flat)
+    return float((O * dO).sum())
+
+
+@pytest.mark.parametrize("L_src,L_ctx,b,alpha_s,alpha_f", [
+    (8, 8, 4, 0.5, 0.5),      # full blocks, both paths
+    (10, 6, 4, 0.5, 0.5),     # partial blocks: weights 4,4,2 | 4,2
+    (8, 12, 4, 0.34, 0.75),   # mostly Taylor
+])
+def test_isa_bwd_finite_differences(L_src, L_ctx, b, alpha_s, alpha_f):
+    rng = np.random.default_rng(31)
+    N, D = L_src + L_ctx, 4
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, D)) for _ in range(4))
+    d = orc.decisions_ref(Q, K, L_src, L_ctx, b, alpha_s, alpha_f)
+    assert len(d["flat"][0, 0]) > 0 and len(d["sharp"][0, 0]) > 0
+    sel, flat = d["sel"], d["flat"]
+    dQ, dK, dV = orc.isa_ref_bwd(Q, K, V, dO, L_src, L_ctx, b, sel, flat)
+    eps = 1e-6
+    for X, G in ((Q, dQ), (K, dK), (V, dV)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            old = X[idx]
+            X[idx] = old + eps
+            lp = _loss(Q, K, V, dO, L_src, L_ctx, b, sel, flat)
+            X[idx] = old - eps
+            lm = _loss(Q, K, V, dO, L_src, L_ctx, b, sel, flat)
+            X[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        scale = np.abs(num).max()
+        np.testing.assert_allclose(G, num, atol=1e-6 * scale, rtol=0)
+    # unselected context rows get no gradient in K and V
+    s, e, n_src, n_ctx = orc.block_grid(L_src, L_ctx, b)
+    for j in range(n_ctx):
+        if j not in sel[0, 0]:
+            assert not dK[0, 0, s[n_src + j]:e[n_src + j]].any()
+            assert not dV[0, 0, s[n_src + j]:e[n_src + j]].any()
+
+
+def test_dense_bwd_matches_library_autograd():
+    rng = np.random.default_rng(32)
+    Q, K, V, dO = (rng.standard_normal((1, 2, 40, 8)) for _ in range(4))
+    t = [torch.from_numpy(x.copy()).requires_grad_(True) for x in (Q, K, V)]
+    out = F.scaled_dot_product_attention(*t)
+    out.backward(torch.from_numpy(dO))
+    ref = orc.dense_ref_bwd(Q, K, V, dO)
+    for g, x in zip(ref, t):
+        np.testing.assert_allclose(g, x.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def test_isa_bwd_all_kept_all_exact_is_dense_bwd():
+    rng = np.random.default_rng(33)
+    Q, K, V, dO = (rng.standard_normal((1, 2, 64, 8)) for _ in range(4))
+    d = orc.decisions_ref(Q, K, 32, 32, 16, 1.0, 0.0)
+    got = orc.isa_ref_bwd(Q, K, V, dO, 32, 32, 16, d["sel"], d["flat"])
+    for g, r in zip(got, orc.dense_ref_bwd(Q, K, V, dO)):
+        np.testing.assert_allclose(g, r, atol=1e-12, rtol=0)

@@ -1,0 +1,58 @@
+"""The pins must reject plausible mistakes in the oracle.
+
+Each case plants one mistake into a temporary copy of ``oracle/`` (on the
+CPU, never touching the real files) and runs the pin suites against it; at
+least one pin must fail.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    ("coarse scale dropped", "S = (Qc @ Kc.T) / math.sqrt(D)", "S = (Qc @ Kc.T)"),
+    ("context score over all query rows", "return P[:n_src, n_src:].mean(axis=0)",
+     "return P[:, n_src:].mean(axis=0)"),
+    ("TopK keeps the smallest", "order = np.lexsort((j, -np.asarray(c)))",
+     "order = np.lexsort((j, np.asarray(c)))"),
+    ("routing sends the sharpest to Taylor", "order = np.lexsort((i, np.asarray(M)))",
+     "order = np.lexsort((i, -np.asarray(M)))"),
+    ("Taylor block weight dropped",
+     "P = np.exp(S - m) * np.asarray(w_new, dtype=np.float64)[None, :]", "P = np.exp(S - m)"),
+    ("sharpness not centred", "return ((P - 1.0 / N_K) ** 2).mean(axis=1)",
+     "return (P ** 2).mean(axis=1)"),
+    ("K in place of V", "O = (P @ V_new) / l[:, None]", "O = (P @ K_new) / l[:, None]"),
+    ("TopK count floors", "k = math.ceil(alpha_s * n_ctx - _GUARD)", "k = math.floor(alpha_s * n_ctx)"),
+    ("gather indexes source blocks", "parts += [X[starts[n_src + j]:ends[n_src + j]] for j in sel]",
+     "parts += [X[starts[j]:ends[j]] for j in sel]"),
+    ("LSE drops the max", "O = (P @ V_new) / l[:, None]\n    return O, m[:, 0] + np.log(l)",
+     "O = (P @ V_new) / l[:, None]\n    return O, np.log(l)"),
+    ("partial context block overruns", "ends.append(min(L_src + (j + 1) * b, L_src + L_ctx))",
+     "ends.append(L_src + (j + 1) * b)"),
+    ("Taylor scale 1/D", "S = (Qrows @ Kc_new.T) / math.sqrt(D)", "S = (Qrows @ Kc_new.T) / D"),
+    ("Taylor uses the first blocks, not the kept ones",
+     "Kc_new = pool_blocks(Kh, starts[kept], ends[kept])",
+     "Kc_new = pool_blocks(Kh, starts, ends)[:len(kept)]"),
+    ("flat takes the largest M", "flat = np.sort(order[:n_flat]).astype(np.int64)",
+     "flat = np.sort(order[-n_flat:] if n_flat else order[:0]).astype(np.int64)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_reject_planted_mistake(tmp_path, name, old, new):
+    src = open(os.path.join(ROOT, "oracle", "isa_oracle.py")).read()
+    assert src.count(old) == 1, f"mutation anchor missing: {old!r}"
+    for d in ("oracle", "synth", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
+    (tmp_path / "oracle" / "isa_oracle.py").write_text(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"no pin caught the planted mistake: {name}\n{r.stdout[-2000:]}"
