@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the ISA forward on one MI355X.
+
+A step is one whole ISA forward (pooling, coarse map, context pre-selection,
+routing, exact path with the fused gather, 0-th order Taylor path, merge) over
+one batch of seeded synthetic [source | context] input already resident in
+HBM.  Default workload: B=1, H=40, D=128, L_src = L_ctx = 16384 (N = 32768),
+b = 64, alpha_s = 0.25, alpha_f = 0.5, bf16.
+
+Prints ONE JSON line with the latency, the dense-equivalent TFLOP/s
+(4 B H N^2 D / latency), the per-stage times (HIP events recorded between the
+stages on the launch stream, inside the timed region), the roofline of the
+dominant kernel (the exact path), the library's own dense attention on the same
+input, and the fp64 CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "ISA fwd latency (ms) + dense-equiv TFLOP/s at N=32K,H=40,D=128 bf16"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload id (synth.CONFIGS)")
+    ap.add_argument("--alpha-s", type=float, default=None)
+    ap.add_argument("--alpha-f", type=float, default=None)
+    ap.add_argument("--dense-steps", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=3,
+                    help="heads of the workload the CPU oracle runs (0: skip)")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, c, n_heads):
+    """Time the fp64 oracle on the first n_heads heads, extrapolate to the job."""
+    import threadpoolctl
+
+    import oracle as orc
+    from synth import to_f64
+
+    B, H = c["B"], c["H"]
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    for h in range(n_heads):
+        sl = (slice(0, 1), slice(h, h + 1))
+        orc.isa_ref(to_f64(inp["q"][sl], "bf16"), to_f64(inp["k"][sl], "bf16"),
+                    to_f64(inp["v"][sl], "bf16"), c["L_src"], c["L_ctx"], c["block"],
+                    c["alpha_s"], c["alpha_f"])
+    dt = time.perf_counter() - t0
+    per_job_s = dt / n_heads * (B * H)
+    N = c["L_src"] + c["L_ctx"]
+    dense_flops = 4.0 * B * H * N * N * c["D"]
+    return {"value": dense_flops / per_job_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+            "cores": int(threads), "kind": "oracle",
+            "latency_ms_extrapolated": per_job_s * 1e3,
+            "sample": f"isa_ref (fp64 NumPy) on {n_heads} of {B * H} heads of the same input, "
+                      f"{dt:.1f} s, extrapolated linearly to all heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (ISA is independent per head; see the sharding "
+              f"note in DESIGN.md); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_context_block_amd as isa
+    from synth import CONFIGS, generate_config
+
+    c = dict(CONFIGS[args.config])
+    if args.alpha_s is not None:
+        c["alpha_s"] = args.alpha_s
+    if args.alpha_f is not None:
+        c["alpha_f"] = args.alpha_f
+    B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
+    N = L_src + L_ctx
+    _log(f"workload {c['name']} B{B} H{H} N{N} D{D} as{c['alpha_s']} af{c['alpha_f']}")
+    t0 = time.perf_counter()
+    inp = generate_config(args.config)
+    _log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+
+    dev = torch.device("cuda:0")
+    to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_gpu(inp["q"]), to_gpu(inp["k"]), to_gpu(inp["v"])
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"])
+    info = plan.info
+    ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    for _ in range(args.warmup):
+        isa.isa_forward(plan, q, k, v, o, lse, workspace=ws)
+    torch.cuda.synchronize()
+    _log("warmup done")
+
+    n_ev = isa.ISA_PROFILE_STAGES + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    for evs in events:
+        for ev in evs:
+            ev.record()  # creates the hipEvent_t before the timed region
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        isa.isa_forward(plan, q, k, v, o, lse, workspace=ws, events=events[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stage_ms = {name: float(np.mean([evs[j].elapsed_time(evs[j + 1]) for evs in events]))
+                for j, name in enumerate(isa.STAGE_NAMES)}
+    _log(f"ISA forward {ms:.3f} ms/step; stages {stage_ms}")
+
+    dense = None
+    if not args.no_dense:
+        od = torch.empty_like(q)
+        lsed = torch.empty_like(lse)
+        for _ in range(2):
+            isa.isa_dense_forward(q, k, v, od, lsed)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.dense_steps):
+            isa.isa_dense_forward(q, k, v, od, lsed)
+        s1.record()
+        torch.cuda.synchronize()
+        dms = s0.elapsed_time(s1) / args.dense_steps
+        dense = {"ms": dms, "tflops": 4.0 * B * H * N * N * D / (dms * 1e-3) / 1e12,
+                 "mfma_frac": 4.0 * B * H * N * N * D / (dms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        _log(f"dense {dms:.3f} ms")
+        del od, lsed
+
+    dense_equiv = 4.0 * B * H * N * N * D
+    exact_flops = 4.0 * B * H * info["n_sharp"] * b * info["l_new"] * D
+    taylor_flops = 4.0 * B * H * info["n_flat"] * b * info["n_kv_blocks"] * D
+    pool_bytes = 3.0 * B * H * N * D * 2 + B * H * info["n_q_blocks"] * D * (8 + 8 + 2 + 2)
+    ex_ms = stage_ms["attn_exact"]
+    achieved = exact_flops / (ex_ms * 1e-3) / 1e12
+    roofline = {"kernel": "attn_fwd_bf16_kernel<128> (exact path)", "bound": "mfma",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flops_per_launch": exact_flops, "avg_launch_ms": ex_ms}
+    stages = {
+        "pool": {"ms": stage_ms["pool"], "GB/s": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9,
+                 "hbm_frac": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "coarse_rowstats": {"ms": stage_ms["coarse_rowstats"]},
+        "coarse_colsum": {"ms": stage_ms["coarse_colsum"]},
+        "select_route": {"ms": stage_ms["select_route"]},
+        "attn_exact": {"ms": ex_ms, "TFLOP/s": achieved, "mfma_frac": achieved / PEAK_BF16_TFLOPS},
+        "attn_taylor": {"ms": stage_ms["attn_taylor"],
+                        "TFLOP/s": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12},
+    }
+    cpu = None
+    if args.cpu_heads > 0:
+        _log(f"CPU oracle on {args.cpu_heads} heads")
+        cpu = cpu_baseline(inp, c, args.cpu_heads)
+    line = {
+        "metric": METRIC, "value": dense_equiv / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent: 4*B*H*N^2*D / ISA latency)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "latency_ms": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded [source|context] generator)",
+        "config": {"workload": c["name"], "B": B, "H": H, "N": N, "L_src": L_src, "L_ctx": L_ctx,
+                   "D": D, "block": b, "alpha_s": c["alpha_s"], "alpha_f": c["alpha_f"],
+                   "k": info["k"], "l_new": info["l_new"], "n_flat": info["n_flat"],
+                   "n_sharp": info["n_sharp"]},
+        "stages": stages,
+        "dense_baseline": dense,
+        "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

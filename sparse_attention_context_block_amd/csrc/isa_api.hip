@@ -1,0 +1,334 @@
+// C-ABI host layer: plan validation, workspace layout and the launch
+// sequence of the ISA forward ([notes] overall framework: pooling attention,
+// Context Pre-Selection, grouping by query sharpness, the exact and the 0-th
+// order Taylor paths, merge).  Host code only; every step of the path runs in
+// the device kernels of the other files.
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "isa_internal.h"
+
+using namespace isa;
+
+struct WorkspaceLayout {
+  size_t qc, kc, kc_lp, vc_lp, rowmax, rowsum, sharpness, ctx_score, sel, flat, sharp, kv_tab;
+  size_t total;
+};
+
+struct isa_plan_s {
+  isa_plan_desc_t d;
+  isa_plan_info_t info;
+  WorkspaceLayout ws;
+  int64_t N;
+  int32_t BH;
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+isa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return ISA_OK;
+  g_last_hip_error = (int)e;
+  return ISA_ERR_HIP;
+}
+
+#define ISA_LAUNCH(expr)                        \
+  do {                                          \
+    isa_status_t s_ = hip_status((expr));       \
+    if (s_ != ISA_OK) return s_;                \
+  } while (0)
+
+size_t elt_size(isa_dtype_t t) { return t == ISA_DTYPE_BF16 ? 2 : 4; }
+
+// Context blocks kept: ceil(alpha_s * n_ctx); query blocks sent to the Taylor
+// path: floor(alpha_f * n_q).  The 1e-6 guard keeps a product that is an
+// integer up to double rounding on that integer.
+int64_t select_count(double alpha_s, int64_t n_ctx) {
+  int64_t k = (int64_t)ceil(alpha_s * (double)n_ctx - 1e-6);
+  return k < 0 ? 0 : (k > n_ctx ? n_ctx : k);
+}
+int64_t flat_count(double alpha_f, int64_t n_q) {
+  int64_t n = (int64_t)floor(alpha_f * (double)n_q + 1e-6);
+  return n < 0 ? 0 : (n > n_q ? n_q : n);
+}
+
+bool ratio_ok(double a) { return a >= 0.0 && a <= 1.0; }  // false for NaN
+
+}  // namespace
+
+extern "C" {
+
+const char* isa_status_string(isa_status_t s) {
+  switch (s) {
+    case ISA_OK: return "ISA_OK";
+    case ISA_ERR_INVALID_ARG: return "ISA_ERR_INVALID_ARG: invalid argument";
+    case ISA_ERR_UNSUPPORTED: return "ISA_ERR_UNSUPPORTED: valid but not supported by this build";
+    case ISA_ERR_WORKSPACE: return "ISA_ERR_WORKSPACE: workspace missing or too small";
+    case ISA_ERR_HIP: return "ISA_ERR_HIP: a HIP call failed";
+  }
+  return "ISA_ERR_UNKNOWN: unknown status";
+}
+
+int isa_last_hip_error(void) { return g_last_hip_error; }
+
+isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
+  if (!out || !desc) return ISA_ERR_INVALID_ARG;
+  *out = nullptr;
+  const isa_plan_desc_t d = *desc;
+  if (d.B < 0 || d.H < 0 || d.D < 1 || d.block < 1 || d.L_src < 1 || d.L_ctx < 0)
+    return ISA_ERR_INVALID_ARG;
+  if (!ratio_ok(d.alpha_s) || !ratio_ok(d.alpha_f) || !ratio_ok(d.alpha_ns))
+    return ISA_ERR_INVALID_ARG;
+  if (d.dtype != ISA_DTYPE_BF16 && d.dtype != ISA_DTYPE_FP32) return ISA_ERR_INVALID_ARG;
+  if ((int64_t)d.L_src + d.L_ctx > INT32_MAX / 2) return ISA_ERR_UNSUPPORTED;
+  if (d.block != kBlock || (d.D != 64 && d.D != 128)) return ISA_ERR_UNSUPPORTED;
+  if (d.L_src % kBlock != 0 || d.L_ctx % kBlock != 0) return ISA_ERR_UNSUPPORTED;
+  if (d.alpha_ns != 0.0) return ISA_ERR_UNSUPPORTED;
+  const int64_t BH = (int64_t)d.B * d.H;
+  if (BH > 65535) return ISA_ERR_UNSUPPORTED;
+
+  isa_plan_s* p = new (std::nothrow) isa_plan_s;
+  if (!p) return ISA_ERR_INVALID_ARG;
+  memset(p, 0, sizeof(*p));
+  p->d = d;
+  p->BH = (int32_t)BH;
+  p->N = (int64_t)d.L_src + d.L_ctx;
+  isa_plan_info_t& in = p->info;
+  in.n_src_blocks = (d.L_src + d.block - 1) / d.block;
+  in.n_ctx_blocks = (d.L_ctx + d.block - 1) / d.block;
+  in.n_q_blocks = in.n_src_blocks + in.n_ctx_blocks;
+  if (in.n_q_blocks > kMaxBlocksPerHead) {
+    delete p;
+    return ISA_ERR_UNSUPPORTED;
+  }
+  in.k = select_count(d.alpha_s, in.n_ctx_blocks);
+  in.n_kv_blocks = in.n_src_blocks + in.k;
+  in.l_new = (int64_t)d.L_src + in.k * d.block;
+  in.n_flat = flat_count(d.alpha_f, in.n_q_blocks);
+  in.n_sharp = in.n_q_blocks - in.n_flat;
+
+  WorkspaceLayout& w = p->ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t pooled = (size_t)BH * in.n_q_blocks * d.D;
+  w.qc = take(pooled * sizeof(double));
+  w.kc = take(pooled * sizeof(double));
+  w.kc_lp = take(pooled * elt_size(d.dtype));
+  w.vc_lp = take(pooled * elt_size(d.dtype));
+  w.rowmax = take((size_t)BH * in.n_q_blocks * sizeof(double));
+  w.rowsum = take((size_t)BH * in.n_q_blocks * sizeof(double));
+  w.sharpness = take((size_t)BH * in.n_q_blocks * sizeof(double));
+  w.ctx_score = take((size_t)BH * in.n_ctx_blocks * sizeof(double));
+  w.sel = take((size_t)BH * in.k * sizeof(int32_t));
+  w.flat = take((size_t)BH * in.n_flat * sizeof(int32_t));
+  w.sharp = take((size_t)BH * in.n_sharp * sizeof(int32_t));
+  w.kv_tab = take((size_t)BH * in.n_kv_blocks * sizeof(int32_t));
+  w.total = off;
+  in.workspace_bytes = off;
+  *out = p;
+  return ISA_OK;
+}
+
+isa_status_t isa_plan_get_info(isa_plan_t plan, isa_plan_info_t* info) {
+  if (!plan || !info) return ISA_ERR_INVALID_ARG;
+  *info = plan->info;
+  return ISA_OK;
+}
+
+isa_status_t isa_plan_destroy(isa_plan_t plan) {
+  delete plan;
+  return ISA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+isa_status_t record(void* const* events, int i, hipStream_t s) {
+  if (!events) return ISA_OK;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
+}
+
+isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const void* V, void* O,
+                          float* lse, const isa_aux_t* aux, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events) {
+  if (!plan) return ISA_ERR_INVALID_ARG;
+  if (plan->BH == 0) return ISA_OK;
+  if (!Q || !K || !V || !O) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ISA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < plan->ws.total || !aligned16(workspace))
+    return ISA_ERR_WORKSPACE;
+  const isa_plan_desc_t& d = plan->d;
+  const isa_plan_info_t& in = plan->info;
+  const WorkspaceLayout& L = plan->ws;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  double* qc = reinterpret_cast<double*>(w + L.qc);
+  double* kc = reinterpret_cast<double*>(w + L.kc);
+  void* kc_lp = w + L.kc_lp;
+  void* vc_lp = w + L.vc_lp;
+  double* rowmax = reinterpret_cast<double*>(w + L.rowmax);
+  double* rowsum = reinterpret_cast<double*>(w + L.rowsum);
+  double* sharpness = (aux && aux->sharpness) ? aux->sharpness
+                                              : reinterpret_cast<double*>(w + L.sharpness);
+  double* ctx_score = (aux && aux->ctx_score) ? aux->ctx_score
+                                              : reinterpret_cast<double*>(w + L.ctx_score);
+  int32_t* sel = (aux && aux->sel) ? aux->sel : reinterpret_cast<int32_t*>(w + L.sel);
+  int32_t* flat = (aux && aux->flat) ? aux->flat : reinterpret_cast<int32_t*>(w + L.flat);
+  int32_t* sharp = (aux && aux->sharp) ? aux->sharp : reinterpret_cast<int32_t*>(w + L.sharp);
+  int32_t* kv_tab = reinterpret_cast<int32_t*>(w + L.kv_tab);
+  const int BH = plan->BH, D = d.D, N = (int)plan->N;
+  const int n_q = (int)in.n_q_blocks, n_src = (int)in.n_src_blocks, n_ctx = (int)in.n_ctx_blocks;
+
+  isa_status_t st;
+#define ISA_STAGE(i)                                   \
+  do {                                                 \
+    if ((st = record(events, (i), s)) != ISA_OK) return st; \
+  } while (0)
+  ISA_STAGE(0);
+  // 1. pooling attention: block means, then the coarse map's row statistics
+  //    and sharpness, and the context column means (all fp64)
+  ISA_LAUNCH(launch_pool(Q, K, V, d.dtype, BH, N, D, d.L_src, n_src, n_q, d.block, qc, kc,
+                         kc_lp, vc_lp, s));
+  ISA_STAGE(1);
+  ISA_LAUNCH(launch_coarse_rowstats(qc, kc, BH, n_q, D, rowmax, rowsum, sharpness, s));
+  ISA_STAGE(2);
+  ISA_LAUNCH(launch_coarse_colsum(qc, kc, rowmax, rowsum, BH, n_q, n_src, n_ctx, D, ctx_score,
+                                  s));
+  ISA_STAGE(3);
+  // 2-3. TopK of the context blocks (block table of K_new) and routing
+  ISA_LAUNCH(launch_select_route(ctx_score, sharpness, BH, n_src, n_ctx, n_q, (int)in.k,
+                                 (int)in.n_flat, sel, flat, sharp, kv_tab, s));
+  ISA_STAGE(4);
+
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  // 4a. exact path: sharp query blocks over the rows of K_new
+  AttnParams pe;
+  memset(&pe, 0, sizeof(pe));
+  pe.q = Q;
+  pe.k = K;
+  pe.v = V;
+  pe.o = O;
+  pe.lse = lse;
+  pe.q_tab = sharp;
+  pe.q_tab_stride = in.n_sharp;
+  pe.n_q_entries = (int)in.n_sharp;
+  pe.kv_tab = kv_tab;
+  pe.kv_tab_stride = in.n_kv_blocks;
+  pe.kv_rows = (int)in.l_new;
+  pe.kv_row_shift = 6;
+  pe.q_head_stride = plan->N * D;
+  pe.kv_head_stride = plan->N * D;
+  pe.lse_head_stride = plan->N;
+  pe.BH = BH;
+  pe.D = D;
+  pe.scale_log2 = scale_log2;
+  pe.lse_offset = 0.0f;
+  ISA_LAUNCH(launch_attention(pe, d.dtype, s));
+  ISA_STAGE(5);
+
+  // 4b. 0-th order Taylor path: flat query blocks over the block means of the
+  //     K_new blocks; every block holds b tokens, weight b
+  AttnParams pt = pe;
+  pt.k = kc_lp;
+  pt.v = vc_lp;
+  pt.q_tab = flat;
+  pt.q_tab_stride = in.n_flat;
+  pt.n_q_entries = (int)in.n_flat;
+  pt.kv_rows = (int)in.n_kv_blocks;
+  pt.kv_row_shift = 0;
+  pt.kv_head_stride = (int64_t)n_q * D;
+  pt.lse_offset = (float)log((double)d.block);
+  ISA_LAUNCH(launch_attention(pt, d.dtype, s));
+  ISA_STAGE(6);
+#undef ISA_STAGE
+  return ISA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+isa_status_t isa_forward(isa_plan_t plan, const void* Q, const void* K, const void* V, void* O,
+                         float* lse, const isa_aux_t* aux, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return forward_impl(plan, Q, K, V, O, lse, aux, workspace, workspace_bytes, stream, nullptr);
+}
+
+isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K, const void* V,
+                                  void* O, float* lse, const isa_aux_t* aux, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return ISA_ERR_INVALID_ARG;
+  return forward_impl(plan, Q, K, V, O, lse, aux, workspace, workspace_bytes, stream, events);
+}
+
+isa_status_t isa_gather(isa_plan_t plan, const void* K, const void* V, const int32_t* sel,
+                        void* K_new, void* V_new, void* stream) {
+  if (!plan) return ISA_ERR_INVALID_ARG;
+  if (plan->BH == 0) return ISA_OK;
+  if (!K || !V || !K_new || !V_new || (!sel && plan->info.k > 0)) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(K_new) || !aligned16(V_new))
+    return ISA_ERR_INVALID_ARG;
+  const isa_plan_desc_t& d = plan->d;
+  ISA_LAUNCH(launch_gather(K, V, sel, d.dtype, plan->BH, (int)plan->N, d.D,
+                           (int)plan->info.n_src_blocks, (int)plan->info.k, d.block, K_new, V_new,
+                           static_cast<hipStream_t>(stream)));
+  return ISA_OK;
+}
+
+isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_dtype_t dtype,
+                               const void* Q, const void* K, const void* V, void* O, float* lse,
+                               void* stream) {
+  if (B < 0 || H < 0 || N < 0 || D < 1) return ISA_ERR_INVALID_ARG;
+  if (dtype != ISA_DTYPE_BF16 && dtype != ISA_DTYPE_FP32) return ISA_ERR_INVALID_ARG;
+  if ((int64_t)B * H == 0 || N == 0) return ISA_OK;
+  if (!Q || !K || !V || !O) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ISA_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128) || N % kBlock != 0 || (int64_t)B * H > 65535)
+    return ISA_ERR_UNSUPPORTED;
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = lse;
+  p.n_q_entries = N / kBlock;
+  p.kv_rows = N;
+  p.kv_row_shift = 0;
+  p.q_head_stride = (int64_t)N * D;
+  p.kv_head_stride = (int64_t)N * D;
+  p.lse_head_stride = N;
+  p.BH = B * H;
+  p.D = D;
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  ISA_LAUNCH(launch_attention(p, dtype, static_cast<hipStream_t>(stream)));
+  return ISA_OK;
+}
+
+size_t isa_backward_workspace_bytes(isa_plan_t plan) {
+  (void)plan;
+  return 0;
+}
+
+isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
+                          const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
+                          void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  (void)Q; (void)K; (void)V; (void)O; (void)dO; (void)lse; (void)aux; (void)dQ; (void)dK;
+  (void)dV; (void)workspace; (void)workspace_bytes; (void)stream;
+  if (!plan) return ISA_ERR_INVALID_ARG;
+  return ISA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

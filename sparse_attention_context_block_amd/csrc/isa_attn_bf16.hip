@@ -1,0 +1,307 @@
+// bf16 MFMA online-softmax attention for gfx950: the exact path of ISA, its
+// 0-th order Taylor path and the dense baseline ([notes] key design 2 gives
+// both update rules: the exact branch accumulates l += rowsum(exp(S)),
+// O += exp(S) V; the representative branch uses K^c_j, V^c_j in place of the
+// whole block with l and O scaled by the block length; both end with O / l).
+//
+// The two paths differ only in where their keys come from, which the
+// AttnParams block table expresses:
+//   exact:  keys = rows of K_new, read through the block table
+//           (source blocks, then the selected context blocks): the gather +
+//           concat of Context Pre-Selection is fused into the tile loads;
+//   Taylor: keys = the pooled K^c_j, V^c_j of the same blocks (one table
+//           entry per row); every block of a full-block grid has the same
+//           weight b, which cancels in O / l and adds ln b to the LSE.
+//
+// Work decomposition (CDNA4, wave64):
+//   workgroup = 4 waves = 128 query rows (two 64-row query blocks of a
+//   worklist); each wave owns 32 query rows.  Keys stream in 64-row tiles
+//   through double-buffered LDS (K row-major, V transposed).
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on the M axis): every lane
+//   then holds 16 scores of ONE query per 32-key subtile, so the row max and
+//   row sum need one permlane32 swap instead of a 32-lane reduction.
+//   O^T += V^T P^T, again 32x32x16 MFMA: the P^T operand is built in
+//   registers straight from the S^T accumulators; the key order inside each
+//   16-key chunk this implies is undone by the order V^T is written to LDS.
+//   Softmax in the exp2 domain; the running max is only raised when a tile
+//   exceeds it by more than 2^8, so the O rescale is skipped for almost
+//   every tile (exact: the same max is used in numerator and denominator).
+//   Query blocks of a head are mapped to one XCD so its keys stay in that
+//   XCD's L2.
+#include "isa_internal.h"
+
+namespace isa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBN = 64;          // keys per tile
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+__device__ inline uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
+  // select the low or high bf16 of two words into one word
+  return high ? ((lo_word >> 16) | (hi_word & 0xffff0000u))
+              : ((lo_word & 0xffffu) | (hi_word << 16));
+}
+
+template <int D>
+struct Smem {
+  static constexpr int kKStride = D * 2 + 16;    // bytes per K row (padded)
+  static constexpr int kVStride = kBN * 2 + 16;  // bytes per V^T row (padded)
+  static constexpr int kKBytes = kBN * kKStride;
+  static constexpr int kVBytes = D * kVStride;
+  static constexpr int kStage = kKBytes + kVBytes;
+  static constexpr int kTotal = 2 * kStage;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p) {
+  using S = Smem<D>;
+  constexpr int KC = D / 8;      // 16-byte chunks per K row
+  constexpr int KCH = kBN * KC / kThreads;  // K chunks per thread per tile
+  constexpr int NKK = D / 16;    // k-steps of the S MFMA
+  constexpr int ND = D / 32;     // d subtiles of O
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::kTotal];
+
+  // ---- XCD-aware mapping of workgroups to (head, query tile) ----
+  const int wg_per_head = (p.n_q_entries + 1) / 2;
+  const int total = wg_per_head * p.BH;
+  const int per_xcd = (total + 7) / 8;
+  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lid >= total) return;
+  const int64_t bh = lid / wg_per_head;
+  const int qt = lid % wg_per_head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- this wave's 32 query rows ----
+  const int e = qt * 2 + (wave >> 1);
+  const bool wave_valid = e < p.n_q_entries;
+  const int qblk = wave_valid ? (p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e) : 0;
+  const int64_t qrow = (int64_t)qblk * kBlock + (wave & 1) * 32 + l32;
+  const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
+  bf16x8_t qreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qreg[kk] = *reinterpret_cast<const bf16x8_t*>(Qh + qrow * D + 16 * kk + 8 * hi);
+
+  // ---- key source rows ----
+  const bf16_bits* Kh = static_cast<const bf16_bits*>(p.k) + bh * p.kv_head_stride;
+  const bf16_bits* Vh = static_cast<const bf16_bits*>(p.v) + bh * p.kv_head_stride;
+  const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
+  const int shift = p.kv_row_shift;
+  const int rmask = (1 << shift) - 1;
+  auto src_row = [&](int r) -> int64_t {
+    r = min(r, p.kv_rows - 1);  // rows past the end are loaded valid, then masked
+    if (!tab) return r;
+    return ((int64_t)tab[r >> shift] << shift) + (r & rmask);
+  };
+
+  // staging registers for the next tile
+  uint4 kst[KCH];
+  uint4 vst[4];
+  // K: chunk c = tid + 256 i -> row c / KC, column chunk c % KC
+  // V: thread -> d chunk vd = tid % KC (8 dims), key group vg = tid / KC (4 keys)
+  const int vd = tid % KC;
+  const int vg = tid / KC;
+  const bool v_active = vg < kBN / 4;
+
+  auto load_tile = [&](int t) {
+    const int base = t * kBN;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + kThreads * i;
+      const int64_t row = src_row(base + c / KC);
+      kst[i] = *reinterpret_cast<const uint4*>(Kh + row * D + (c % KC) * 8);
+    }
+    if (v_active) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = src_row(base + 4 * vg + i);
+        vst[i] = *reinterpret_cast<const uint4*>(Vh + row * D + vd * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* ks = smem + buf * S::kStage;
+    unsigned char* vs = ks + S::kKBytes;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4*>(ks + (c / KC) * S::kKStride + (c % KC) * 16) = kst[i];
+    }
+    if (v_active) {
+      // keys 4vg..4vg+3 sit in 16-key chunk vg/4 at quad q = vg%4; inside a chunk
+      // the PV operand wants quad order (0, 2, 1, 3): position quad = swap of q's bits
+      const int q = vg & 3;
+      const int pos = (vg >> 2) * 16 + (((q & 1) << 1) | (q >> 1)) * 4;
+      const uint32_t w[4][4] = {{vst[0].x, vst[0].y, vst[0].z, vst[0].w},
+                                {vst[1].x, vst[1].y, vst[1].z, vst[1].w},
+                                {vst[2].x, vst[2].y, vst[2].z, vst[2].w},
+                                {vst[3].x, vst[3].y, vst[3].z, vst[3].w}};
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const bool h = dd & 1;
+        const int wi = dd >> 1;
+        uint2 out;
+        out.x = pack2(w[0][wi], w[1][wi], h);
+        out.y = pack2(w[2][wi], w[3][wi], h);
+        *reinterpret_cast<uint2*>(vs + (vd * 8 + dd) * S::kVStride + pos * 2) = out;
+      }
+    }
+  };
+
+  f32x16_t oacc[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[j][r] = 0.0f;
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  const float sl2 = p.scale_log2;
+  const int n_tiles = (p.kv_rows + kBN - 1) / kBN;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const unsigned char* ks = smem + buf * S::kStage;
+    const unsigned char* vs = ks + S::kKBytes;
+
+    // S^T (64 keys x 32 queries) = K_tile Q^T
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[s][r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            ks + (32 * s + l32) * S::kKStride + (16 * kk + 8 * hi) * 2);
+        sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[s], 0, 0, 0);
+      }
+    }
+
+    // mask keys past the end (last tile of the Taylor path only)
+    const int valid = p.kv_rows - t * kBN;
+    if (valid < kBN) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= valid) sacc[s][r] = -INFINITY;
+        }
+    }
+
+    // online softmax (exp2 domain); lane and lane^32 hold the same query
+    float tmax = sacc[0][0];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[s][r]);
+    {
+      // the swap returns {own, partner} in an order that depends on the half
+      // of the wave, so take both
+      const uint32_t u = __float_as_uint(tmax);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float tmax_s = tmax * sl2;
+    if (__builtin_amdgcn_ballot_w64(tmax_s > m_run + kRescaleThreshold) != 0) {
+      const float m_new = fmaxf(m_run, tmax_s);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[j][r] *= alpha;
+      m_run = m_new;
+    }
+
+    bf16x8_t pk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int e2 = 0; e2 < 8; e2 += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e2], sl2, -m_run));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e2 + 1], sl2, -m_run));
+        bf16x2_t pr;
+        pr[0] = (__bf16)p0;
+        pr[1] = (__bf16)p1;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+        pk[c][e2] = pr[0];
+        pk[c][e2 + 1] = pr[1];
+      }
+    }
+
+    // O^T (D x 32 queries) += V^T P^T
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int j = 0; j < ND; ++j) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            vs + (32 * j + l32) * S::kVStride + (16 * c + 8 * hi) * 2);
+        oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[j], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l, bf16 round-to-nearest-even, LSE ----
+  {
+    const uint32_t u = __float_as_uint(l_run);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // own + partner
+  }
+  if (!wave_valid) return;
+  const float inv = 1.0f / l_run;
+  bf16_bits* Oh = static_cast<bf16_bits*>(p.o) + bh * p.q_head_stride + qrow * D;
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x2_t a, b;
+      a[0] = (__bf16)(oacc[j][4 * g + 0] * inv);
+      a[1] = (__bf16)(oacc[j][4 * g + 1] * inv);
+      b[0] = (__bf16)(oacc[j][4 * g + 2] * inv);
+      b[1] = (__bf16)(oacc[j][4 * g + 3] * inv);
+      uint2 w;
+      w.x = __builtin_bit_cast(uint32_t, a);
+      w.y = __builtin_bit_cast(uint32_t, b);
+      *reinterpret_cast<uint2*>(Oh + 32 * j + 8 * g + 4 * hi) = w;
+    }
+  }
+  if (p.lse && hi == 0) {
+    p.lse[bh * p.lse_head_stride + qrow] =
+        (m_run + __log2f(l_run)) * 0.69314718055994531f + p.lse_offset;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
+  if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;
+  const int wg_per_head = (p.n_q_entries + 1) / 2;
+  const int64_t total = (int64_t)wg_per_head * p.BH;
+  const int64_t grid = ((total + 7) / 8) * 8;
+  if (p.D == 128)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       p);
+  return hipGetLastError();
+}
+
+}  // namespace isa

@@ -1,0 +1,77 @@
+// Internal declarations shared by the ISA kernels and the C-ABI host layer.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "isa.h"
+
+namespace isa {
+
+typedef uint16_t bf16_bits;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// Block length the device kernels are built for (tokens per pooled block;
+// also the key-tile height of the attention kernels).
+constexpr int kBlock = 64;
+
+// ---------------------------------------------------------------------------
+// Attention launch description shared by the exact path, the 0-th order
+// Taylor path and the dense baseline.  Queries come in 64-row blocks listed in
+// q_tab (NULL: block e is block e); keys/values are the rows of a virtual
+// K_new whose row r lives at source row
+//     kv_tab[r >> kv_row_shift] * 2^kv_row_shift + (r & (2^kv_row_shift - 1))
+// of the per-head K/V arrays (kv_tab NULL: row r is row r).
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                // may be null
+  const int32_t* q_tab;      // [BH][q_tab_stride] or null
+  int64_t q_tab_stride;
+  int32_t n_q_entries;       // 64-row query blocks per head
+  const int32_t* kv_tab;     // [BH][kv_tab_stride] or null
+  int64_t kv_tab_stride;
+  int32_t kv_rows;           // rows of the virtual K_new per head (>= 1)
+  int32_t kv_row_shift;      // 6 (entries name 64-row blocks) or 0 (entries name rows)
+  int64_t q_head_stride;     // elements between heads of Q and O
+  int64_t kv_head_stride;    // elements between heads of the K/V arrays
+  int64_t lse_head_stride;   // floats between heads of lse
+  int32_t BH;
+  int32_t D;
+  float scale_log2;          // log2(e) / sqrt(D)
+  float lse_offset;          // added to every lse (ln of a uniform block weight)
+};
+
+hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream);
+
+hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t dtype,
+                       int BH, int N, int D, int L_src, int n_src, int n_q, int block,
+                       double* qc, double* kc, void* kc_lp, void* vc_lp, hipStream_t stream);
+
+hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
+                                  double* rowmax, double* rowsum, double* sharpness,
+                                  hipStream_t stream);
+
+hipError_t launch_coarse_colsum(const double* qc, const double* kc, const double* rowmax,
+                                const double* rowsum, int BH, int n_q, int n_src, int n_ctx,
+                                int D, double* ctx_score, hipStream_t stream);
+
+hipError_t launch_select_route(const double* ctx_score, const double* sharpness, int BH,
+                               int n_src, int n_ctx, int n_q, int k, int n_flat,
+                               int32_t* sel, int32_t* flat, int32_t* sharp, int32_t* kv_tab,
+                               hipStream_t stream);
+
+hipError_t launch_gather(const void* K, const void* V, const int32_t* sel, isa_dtype_t dtype,
+                         int BH, int N, int D, int n_src, int k, int block,
+                         void* K_new, void* V_new, hipStream_t stream);
+
+// Largest number of query blocks the selection kernel handles per head.
+constexpr int kMaxBlocksPerHead = 4096;
+
+}  // namespace isa

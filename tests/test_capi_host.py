@@ -1,0 +1,143 @@
+"""C-ABI host tests (CPU only): the library loads, exports every symbol the
+header declares, and plan creation validates and sizes problems without any
+HIP call.  No compute entry point is called here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as orc
+import sparse_attention_context_block_amd as isa
+from synth import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(isa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(isa.LIB_PATH)
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in include/isa.h but not exported"
+    assert sorted(isa.EXPORTS) == declared
+
+
+def test_status_strings():
+    for s in range(5):
+        assert isa.isa_status_string(s).startswith("ISA_")
+    assert "UNKNOWN" in isa.isa_status_string(99)
+    assert isa.isa_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_plan_info_matches_oracle_counts(cfg):
+    c = CONFIGS[cfg]
+    dt = "bf16" if c["dtype"] == "bf16" else "fp32"
+    import torch
+    p = isa.isa_plan_create(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"],
+                            c["alpha_s"], c["alpha_f"],
+                            dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+    info = p.info
+    starts, ends, n_src, n_ctx = orc.block_grid(c["L_src"], c["L_ctx"], c["block"])
+    n_q = len(starts)
+    k = orc.select_count(c["alpha_s"], n_ctx)
+    n_flat = orc.flat_count(c["alpha_f"], n_q)
+    assert (info["n_src_blocks"], info["n_ctx_blocks"], info["n_q_blocks"]) == (n_src, n_ctx, n_q)
+    assert info["k"] == k and info["n_kv_blocks"] == n_src + k
+    assert info["l_new"] == c["L_src"] + k * c["block"]
+    assert info["n_flat"] == n_flat and info["n_sharp"] == n_q - n_flat
+    assert info["workspace_bytes"] > 0
+
+
+def test_plan_counts_at_headline_shape():
+    p = isa.isa_plan_create(1, 40, 16384, 16384, 128, 64, 0.25, 0.5)
+    assert p.info["k"] == 64 and p.info["n_kv_blocks"] == 320 and p.info["l_new"] == 20480
+    assert p.info["n_flat"] == 256 and p.info["n_sharp"] == 256
+
+
+@pytest.mark.parametrize("alpha_s,alpha_f", [(0.125, 0.25), (0.25, 0.5), (0.5, 0.75),
+                                             (0.0, 0.0), (1.0, 1.0), (0.1, 0.3), (0.33, 0.66)])
+def test_plan_counts_follow_the_rounding_rule(alpha_s, alpha_f):
+    p = isa.isa_plan_create(1, 2, 25600, 25600, 128, 64, alpha_s, alpha_f)
+    assert p.info["k"] == orc.select_count(alpha_s, 400)
+    assert p.info["n_flat"] == orc.flat_count(alpha_f, 800)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), isa.ISA_ERR_INVALID_ARG),
+    (dict(H=-2), isa.ISA_ERR_INVALID_ARG),
+    (dict(D=0), isa.ISA_ERR_INVALID_ARG),
+    (dict(L_src=0), isa.ISA_ERR_INVALID_ARG),
+    (dict(L_ctx=-64), isa.ISA_ERR_INVALID_ARG),
+    (dict(block=0), isa.ISA_ERR_INVALID_ARG),
+    (dict(alpha_s=1.5), isa.ISA_ERR_INVALID_ARG),
+    (dict(alpha_f=-0.1), isa.ISA_ERR_INVALID_ARG),
+    (dict(alpha_s=float("nan")), isa.ISA_ERR_INVALID_ARG),
+    (dict(block=32), isa.ISA_ERR_UNSUPPORTED),
+    (dict(D=96), isa.ISA_ERR_UNSUPPORTED),
+    (dict(L_src=100), isa.ISA_ERR_UNSUPPORTED),
+    (dict(L_ctx=70), isa.ISA_ERR_UNSUPPORTED),
+    (dict(alpha_ns=0.0625), isa.ISA_ERR_UNSUPPORTED),
+    (dict(L_src=64 * 4097, L_ctx=0), isa.ISA_ERR_UNSUPPORTED),
+])
+def test_plan_validation(kw, status):
+    args = dict(B=1, H=2, L_src=256, L_ctx=256, D=128, block=64, alpha_s=0.5, alpha_f=0.5)
+    args.update(kw)
+    with pytest.raises(isa.IsaError) as e:
+        isa.isa_plan_create(**args)
+    assert e.value.status == status
+
+
+def test_null_arguments_rejected_before_any_launch():
+    lib = isa._lib()
+    assert lib.isa_plan_create(None, None) == isa.ISA_ERR_INVALID_ARG
+    assert lib.isa_plan_get_info(None, None) == isa.ISA_ERR_INVALID_ARG
+    assert lib.isa_plan_destroy(None) == isa.ISA_OK
+    p = isa.isa_plan_create(1, 2, 256, 256, 128)
+    # null tensors / workspace: rejected on the host, nothing launched
+    assert lib.isa_forward(p.handle, None, None, None, None, None, None, None, 0, None) \
+        == isa.ISA_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.isa_forward(p.handle, fake, fake, fake, fake, None, None, None, 0, None) \
+        == isa.ISA_ERR_WORKSPACE
+    assert lib.isa_forward(p.handle, fake, fake, fake, fake, None, None, fake, 16, None) \
+        == isa.ISA_ERR_WORKSPACE
+    misaligned = ctypes.c_void_p(0x1004)
+    assert lib.isa_forward(p.handle, misaligned, fake, fake, fake, None, None, fake, 1 << 40,
+                           None) == isa.ISA_ERR_INVALID_ARG
+    assert lib.isa_forward(None, fake, fake, fake, fake, None, None, fake, 1 << 40, None) \
+        == isa.ISA_ERR_INVALID_ARG
+    assert lib.isa_gather(p.handle, None, fake, fake, fake, fake, None) == isa.ISA_ERR_INVALID_ARG
+    assert lib.isa_dense_forward(1, 1, 100, 128, 0, fake, fake, fake, fake, None, None) \
+        == isa.ISA_ERR_UNSUPPORTED
+    assert lib.isa_dense_forward(1, 1, 128, 128, 0, None, fake, fake, fake, None, None) \
+        == isa.ISA_ERR_INVALID_ARG
+    assert lib.isa_dense_forward(-1, 1, 128, 128, 0, fake, fake, fake, fake, None, None) \
+        == isa.ISA_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op():
+    lib = isa._lib()
+    p = isa.isa_plan_create(0, 4, 256, 256, 128)
+    assert p.info["workspace_bytes"] >= 0
+    assert lib.isa_forward(p.handle, None, None, None, None, None, None, None, 0, None) == isa.ISA_OK
+    assert lib.isa_dense_forward(0, 3, 128, 128, 0, None, None, None, None, None, None) == isa.ISA_OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    p = isa.isa_plan_create(1, 1, 64, 64, 64)
+    x = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        isa.isa_forward(p, x, x, x)
+    with pytest.raises(TypeError):
+        isa.isa_dense_forward(x, x, x)
