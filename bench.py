@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=3,
                     help="heads of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the run, launch a plain 256 MiB fp32 copy kernel (x2 scale) "
+                         "whose FETCH_SIZE / WRITE_SIZE calibrate the HBM counters")
     return ap.parse_args()
 
 
@@ -72,7 +75,46 @@ def cpu_baseline(inp, c, n_heads):
                       f"{dt:.1f} s, extrapolated linearly to all heads"}
 
 
+def _short(name):
+    name = name.replace("isa::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def summarize(paths):
+    """Summarise rocprofv3 CSVs per (kernel, grid): kernel traces give the
+    average duration; counter collections give the average value per dispatch
+    of every counter.  Prints a text table."""
+    import csv
+    from collections import defaultdict
+
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        print(f"# {path}")
+        if rows and "Counter_Name" in rows[0]:
+            acc = defaultdict(list)
+            for r in rows:
+                key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])
+                acc[key].append(float(r["Counter_Value"]))
+            print(f"{'kernel':56s} {'grid':>10s} {'counter':>26s} {'dispatches':>10s} {'avg':>16s}")
+            for (k, g, c), v in sorted(acc.items()):
+                print(f"{k:56s} {g:10d} {c:>26s} {len(v):10d} {np.mean(v):16.1f}")
+        else:
+            acc = defaultdict(list)
+            for r in rows:
+                key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))
+                acc[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            print(f"{'kernel':56s} {'grid threads':>12s} {'calls':>6s} {'avg us':>10s} "
+                  f"{'min us':>10s} {'max us':>10s}")
+            for (k, g), v in sorted(acc.items(), key=lambda kv: -np.sum(kv[1])):
+                v = np.array(v) / 1e3
+                print(f"{k:56s} {g:12d} {len(v):6d} {v.mean():10.1f} {v.min():10.1f} "
+                      f"{v.max():10.1f}")
+
+
 def main():
+    if len(sys.argv) > 2 and sys.argv[1] == "--summarize":
+        summarize(sys.argv[2:])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (ISA is independent per head; see the sharding "
@@ -188,6 +230,13 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        _log("copy calibration: 2 launches, 268435456 bytes read and written each")
 
 
 if __name__ == "__main__":

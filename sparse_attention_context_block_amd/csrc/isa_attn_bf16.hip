@@ -53,11 +53,12 @@ struct Smem {
   static constexpr int kTotal = 2 * kStage;
 };
 
-template <int D>
+template <int D, bool kRowTable>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   using S = Smem<D>;
   constexpr int KC = D / 8;      // 16-byte chunks per K row
-  constexpr int KCH = kBN * KC / kThreads;  // K chunks per thread per tile
+  constexpr int KCH = kBN * KC / kThreads;  // K chunks per thread per tile (2 or 4)
+  static_assert(KCH == 2 || KCH == 4, "D must be 64 or 128");
   constexpr int NKK = D / 16;    // k-steps of the S MFMA
   constexpr int ND = D / 32;     // d subtiles of O
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::kTotal];
@@ -92,65 +93,91 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const bf16_bits* Kh = static_cast<const bf16_bits*>(p.k) + bh * p.kv_head_stride;
   const bf16_bits* Vh = static_cast<const bf16_bits*>(p.v) + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
-  const int shift = p.kv_row_shift;
-  const int rmask = (1 << shift) - 1;
-  auto src_row = [&](int r) -> int64_t {
-    r = min(r, p.kv_rows - 1);  // rows past the end are loaded valid, then masked
-    if (!tab) return r;
-    return ((int64_t)tab[r >> shift] << shift) + (r & rmask);
+  // A 64-row tile is one contiguous 64-row block of the K/V arrays unless the
+  // table names single rows (the Taylor path): then every row is looked up.
+  const bool row_table = kRowTable;  // launcher: kv_tab set and kv_row_shift == 0
+  const int n_tiles = (p.kv_rows + kBN - 1) / kBN;
+  // block-table entry of the tile to load next, prefetched one tile ahead so
+  // its scalar load latency hides behind a whole tile of compute
+  int next_blk = (tab && !row_table) ? tab[0] : 0;
+  auto tile_row0 = [&](int t) -> int64_t {
+    if (!tab) return (int64_t)t * kBN;
+    if (row_table) return 0;
+    const int64_t r0 = (int64_t)next_blk * kBN;
+    next_blk = (t + 1 < n_tiles) ? tab[t + 1] : 0;
+    return r0;
+  };
+  auto src_row = [&](int64_t row0, int t, int r) -> int64_t {
+    if (!row_table) return row0 + r;  // contiguous (block tiles are always full)
+    return tab[min(t * kBN + r, p.kv_rows - 1)];  // rows past the end: valid, then masked
   };
 
-  // staging registers for the next tile
-  uint4 kst[KCH];
-  uint4 vst[4];
+  // staging registers for the next tile (named, so they stay in VGPRs)
+  uint4 k0, k1, k2, k3;  // K chunks c = tid + 256 i (i < KCH <= 4)
+  uint4 v0, v1, v2, v3;
   // K: chunk c = tid + 256 i -> row c / KC, column chunk c % KC
-  // V: thread -> d chunk vd = tid % KC (8 dims), key group vg = tid / KC (4 keys)
-  const int vd = tid % KC;
-  const int vg = tid / KC;
-  const bool v_active = vg < kBN / 4;
+  // V: thread -> key group vg = tid % 16 (4 keys), d chunk vd = tid / 16 (8 dims).
+  // The key group varies fastest so that the 16 lanes of an LDS write phase
+  // land on 16 different 8-byte bank pairs of one V^T row band (rows 8 apart
+  // share banks, positions inside a row do not).
+  const int vg = tid % (kBN / 4);
+  const int vd = tid / (kBN / 4);
+  const bool v_active = vd < KC;
+  // keys 4vg..4vg+3 sit in 16-key chunk vg/4 at quad q = vg%4; inside a chunk
+  // the PV operand wants quad order (0, 2, 1, 3): position quad = swap of q's bits
+  const int vq = vg & 3;
+  const int vpos = (vg >> 2) * 16 + (((vq & 1) << 1) | (vq >> 1)) * 4;
 
   auto load_tile = [&](int t) {
-    const int base = t * kBN;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int64_t row = src_row(base + c / KC);
-      kst[i] = *reinterpret_cast<const uint4*>(Kh + row * D + (c % KC) * 8);
+    const int64_t row0 = tile_row0(t);
+#define ISA_K_LOAD(I, R)                                                                \
+  {                                                                                     \
+    const int c = tid + kThreads * I;                                                   \
+    R = *reinterpret_cast<const uint4*>(Kh + src_row(row0, t, c / KC) * D + (c % KC) * 8); \
+  }
+    ISA_K_LOAD(0, k0)
+    ISA_K_LOAD(1, k1)
+    if constexpr (KCH > 2) {
+      ISA_K_LOAD(2, k2)
+      ISA_K_LOAD(3, k3)
     }
+#undef ISA_K_LOAD
     if (v_active) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = src_row(base + 4 * vg + i);
-        vst[i] = *reinterpret_cast<const uint4*>(Vh + row * D + vd * 8);
-      }
+      const bf16_bits* vb = Vh + vd * 8;
+      v0 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 0) * D);
+      v1 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 1) * D);
+      v2 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 2) * D);
+      v3 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 3) * D);
     }
   };
   auto store_tile = [&](int buf) {
     unsigned char* ks = smem + buf * S::kStage;
     unsigned char* vs = ks + S::kKBytes;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(ks + (c / KC) * S::kKStride + (c % KC) * 16) = kst[i];
+#define ISA_K_STORE(I, R)                                                                \
+  {                                                                                      \
+    const int c = tid + kThreads * I;                                                    \
+    *reinterpret_cast<uint4*>(ks + (c / KC) * S::kKStride + (c % KC) * 16) = R;          \
+  }
+    ISA_K_STORE(0, k0)
+    ISA_K_STORE(1, k1)
+    if constexpr (KCH > 2) {
+      ISA_K_STORE(2, k2)
+      ISA_K_STORE(3, k3)
     }
+#undef ISA_K_STORE
     if (v_active) {
-      // keys 4vg..4vg+3 sit in 16-key chunk vg/4 at quad q = vg%4; inside a chunk
-      // the PV operand wants quad order (0, 2, 1, 3): position quad = swap of q's bits
-      const int q = vg & 3;
-      const int pos = (vg >> 2) * 16 + (((q & 1) << 1) | (q >> 1)) * 4;
-      const uint32_t w[4][4] = {{vst[0].x, vst[0].y, vst[0].z, vst[0].w},
-                                {vst[1].x, vst[1].y, vst[1].z, vst[1].w},
-                                {vst[2].x, vst[2].y, vst[2].z, vst[2].w},
-                                {vst[3].x, vst[3].y, vst[3].z, vst[3].w}};
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const bool h = dd & 1;
-        const int wi = dd >> 1;
-        uint2 out;
-        out.x = pack2(w[0][wi], w[1][wi], h);
-        out.y = pack2(w[2][wi], w[3][wi], h);
-        *reinterpret_cast<uint2*>(vs + (vd * 8 + dd) * S::kVStride + pos * 2) = out;
-      }
+      unsigned char* vrow = vs + (vd * 8) * S::kVStride + vpos * 2;
+      // word w of a key's 8 dims holds dims 2w (low half) and 2w+1 (high half)
+#define ISA_VT_STORE(W, F)                                                              \
+  *reinterpret_cast<uint2*>(vrow + (2 * W) * S::kVStride) =                            \
+      make_uint2(pack2(v0.F, v1.F, false), pack2(v2.F, v3.F, false));                  \
+  *reinterpret_cast<uint2*>(vrow + (2 * W + 1) * S::kVStride) =                        \
+      make_uint2(pack2(v0.F, v1.F, true), pack2(v2.F, v3.F, true));
+      ISA_VT_STORE(0, x)
+      ISA_VT_STORE(1, y)
+      ISA_VT_STORE(2, z)
+      ISA_VT_STORE(3, w)
+#undef ISA_VT_STORE
     }
   };
 
@@ -162,7 +189,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   float m_run = -INFINITY;
   float l_run = 0.0f;
   const float sl2 = p.scale_log2;
-  const int n_tiles = (p.kv_rows + kBN - 1) / kBN;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   load_tile(0);
@@ -189,9 +215,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
       }
     }
 
-    // mask keys past the end (last tile of the Taylor path only)
+    // mask keys past the end (only a row-table tile can be partial)
     const int valid = p.kv_rows - t * kBN;
-    if (valid < kBN) {
+    if (kRowTable && valid < kBN) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -294,13 +320,19 @@ hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
   if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;
   const int wg_per_head = (p.n_q_entries + 1) / 2;
   const int64_t total = (int64_t)wg_per_head * p.BH;
-  const int64_t grid = ((total + 7) / 8) * 8;
-  if (p.D == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       p);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       p);
+  const dim3 grid((unsigned)(((total + 7) / 8) * 8));
+  const bool row_table = p.kv_tab && p.kv_row_shift == 0;
+  if (p.D == 128) {
+    if (row_table)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (row_table)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
