@@ -316,19 +316,91 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
   return ISA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+  size_t delta, kv_tab, iota, kc, vc, dkc, dvc, total;
+};
+
+BwdLayout bwd_layout(const isa_plan_s* p) {
+  BwdLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t BH = (size_t)p->BH, n_kv = (size_t)p->info.n_kv_blocks, D = (size_t)p->d.D;
+  w.delta = take(BH * (size_t)p->N * sizeof(float));
+  w.kv_tab = take(BH * n_kv * sizeof(int32_t));
+  w.iota = take(n_kv * sizeof(int32_t));
+  w.kc = take(BH * n_kv * D * 2);
+  w.vc = take(BH * n_kv * D * 2);
+  w.dkc = take(BH * n_kv * D * sizeof(float));
+  w.dvc = take(BH * n_kv * D * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t isa_backward_workspace_bytes(isa_plan_t plan) {
-  (void)plan;
-  return 0;
+  if (!plan) return 0;
+  return bwd_layout(plan).total;
 }
 
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  (void)Q; (void)K; (void)V; (void)O; (void)dO; (void)lse; (void)aux; (void)dQ; (void)dK;
-  (void)dV; (void)workspace; (void)workspace_bytes; (void)stream;
   if (!plan) return ISA_ERR_INVALID_ARG;
-  return ISA_ERR_UNSUPPORTED;
+  if (plan->BH == 0) return ISA_OK;
+  const isa_plan_info_t& in = plan->info;
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !aux) return ISA_ERR_INVALID_ARG;
+  if ((in.k > 0 && !aux->sel) || (in.n_flat > 0 && !aux->flat) || (in.n_sharp > 0 && !aux->sharp))
+    return ISA_ERR_INVALID_ARG;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return ISA_ERR_INVALID_ARG;
+  if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
+  const BwdLayout W = bwd_layout(plan);
+  if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  BwdLaunch L;
+  L.BH = plan->BH;
+  L.D = plan->d.D;
+  L.N = (int)plan->N;
+  L.L_src = plan->d.L_src;
+  L.n_src = (int)in.n_src_blocks;
+  L.n_ctx = (int)in.n_ctx_blocks;
+  L.k = (int)in.k;
+  L.n_flat = (int)in.n_flat;
+  L.n_sharp = (int)in.n_sharp;
+  L.Q = static_cast<const bf16_bits*>(Q);
+  L.K = static_cast<const bf16_bits*>(K);
+  L.V = static_cast<const bf16_bits*>(V);
+  L.O = static_cast<const bf16_bits*>(O);
+  L.dO = static_cast<const bf16_bits*>(dO);
+  L.lse = lse;
+  L.sel = aux->sel;
+  L.flat = aux->flat;
+  L.sharp = aux->sharp;
+  L.dQ = static_cast<bf16_bits*>(dQ);
+  L.dK = static_cast<bf16_bits*>(dK);
+  L.dV = static_cast<bf16_bits*>(dV);
+  L.delta = reinterpret_cast<float*>(w + W.delta);
+  L.kv_tab = reinterpret_cast<int32_t*>(w + W.kv_tab);
+  L.iota = reinterpret_cast<int32_t*>(w + W.iota);
+  L.kc = reinterpret_cast<bf16_bits*>(w + W.kc);
+  L.vc = reinterpret_cast<bf16_bits*>(w + W.vc);
+  L.dkc = reinterpret_cast<float*>(w + W.dkc);
+  L.dvc = reinterpret_cast<float*>(w + W.dvc);
+  ISA_LAUNCH(launch_backward(L, static_cast<hipStream_t>(stream)));
+  return ISA_OK;
 }
 
 }  // extern "C"

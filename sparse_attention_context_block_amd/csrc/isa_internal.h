@@ -71,6 +71,23 @@ hipError_t launch_gather(const void* K, const void* V, const int32_t* sel, isa_d
                          int BH, int N, int D, int n_src, int k, int block,
                          void* K_new, void* V_new, hipStream_t stream);
 
+// Backward launch description (bf16 only).  Workspace pointers: delta
+// [BH*N] f32, kv_tab [BH*(n_src+k)] i32, iota [n_src+k] i32, kc/vc
+// [BH*(n_src+k)*D] bf16 (means of the kept blocks), dkc/dvc same shape f32.
+struct BwdLaunch {
+  int BH, D, N, L_src, n_src, n_ctx, k, n_flat, n_sharp;
+  const bf16_bits *Q, *K, *V, *O, *dO;
+  const float* lse;
+  const int32_t *sel, *flat, *sharp;
+  bf16_bits *dQ, *dK, *dV;
+  float* delta;
+  int32_t *kv_tab, *iota;
+  bf16_bits *kc, *vc;
+  float *dkc, *dvc;
+};
+
+hipError_t launch_backward(const BwdLaunch& L, hipStream_t stream);
+
 // Largest number of query blocks the selection kernel handles per head.
 constexpr int kMaxBlocksPerHead = 4096;
 

@@ -1,0 +1,105 @@
+"""GPU parity of the decision-frozen ISA backward against the fp64 oracle.
+
+The forward runs on the GPU first; its decisions (sel, flat, sharp) are given
+to both the GPU backward and the oracle's isa_ref_bwd.  Bars (the pages print
+none; a reading, derived from bf16 operands with fp32 accumulation): for each of
+dQ, dK, dV, relative Frobenius error <= 1e-2 and max-abs error <= 2e-2 of the
+largest reference magnitude.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import sparse_attention_context_block_amd as isa
+from synth import generate, generate_config, CONFIGS, to_f64
+from tests.parity import out_f64, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO, MAX_FRAC = 1e-2, 2e-2
+
+
+def _say(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f):
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, 64, alpha_s, alpha_f)
+    q, k, v, do = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v", "do"))
+    o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
+    dq, dk, dv = isa.isa_backward(plan, q, k, v, o, do, lse, aux)
+    torch.cuda.synchronize()
+    return plan, (dq, dk, dv), {key: t.cpu().numpy() for key, t in aux.items()}
+
+
+def _check_grads(got, ref, what=""):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        g = np.asarray(g, dtype=np.float64)
+        rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+        mx = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
+        assert rel <= REL_FRO and mx <= MAX_FRAC, \
+            f"{what} {name}: rel-Frobenius {rel:.3e} (bar {REL_FRO}), max-abs/max|ref| {mx:.3e}"
+        _say(f"{what} {name}: rel-Frobenius {rel:.2e}, max-abs/max|ref| {mx:.2e}")
+
+
+@pytest.mark.parametrize("B,H,L_src,L_ctx,D,alpha_s,alpha_f,seed", [
+    (1, 2, 512, 512, 128, 0.5, 0.5, 41),
+    (1, 3, 640, 448, 128, 0.25, 0.5, 42),   # 17 blocks: odd worklists, 12 pooled rows
+    (2, 2, 1024, 768, 64, 0.34, 0.3, 43),   # D = 64, B = 2
+    (1, 2, 512, 512, 128, 0.5, 0.0, 44),    # exact path only
+    (1, 2, 512, 512, 128, 0.5, 1.0, 45),    # Taylor path only
+    (1, 2, 512, 512, 128, 0.0, 0.5, 46),    # no context kept
+    (1, 2, 512, 0, 128, 0.5, 0.5, 47),      # no context at all
+])
+def test_backward_small_full_parity(B, H, L_src, L_ctx, D, alpha_s, alpha_f, seed):
+    _say(f"bwd B{B} H{H} L_src{L_src} L_ctx{L_ctx} D{D} as{alpha_s} af{alpha_f} seed{seed}")
+    inp = generate(B, H, L_src, L_ctx, D, 64, seed=seed, variant="icl", grad=True)
+    plan, grads, aux = _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f)
+    ref = orc.isa_ref_bwd(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v", "do")),
+                          L_src, L_ctx, 64, aux["sel"], aux["flat"])
+    _check_grads([out_f64(g) for g in grads], ref, "full")
+    # context rows of blocks that were not kept get exactly zero
+    dk = out_f64(grads[1])
+    for bi in range(B):
+        for h in range(H):
+            for j in range(L_ctx // 64):
+                if j not in aux["sel"][bi, h]:
+                    assert not dk[bi, h, L_src + 64 * j:L_src + 64 * (j + 1)].any()
+
+
+def test_backward_all_kept_all_exact_is_dense_backward():
+    _say("bwd as1 af0 vs dense backward, seed 48")
+    inp = generate(1, 2, 512, 512, 128, 64, seed=48, variant="icl", grad=True)
+    _, grads, _ = _fwd_bwd(inp, 1, 2, 512, 512, 128, 1.0, 0.0)
+    ref = orc.dense_ref_bwd(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v", "do")))
+    _check_grads([out_f64(g) for g in grads], ref, "dense")
+
+
+def test_backward_deterministic():
+    _say("bwd determinism B1 H2 N2048 seed 49")
+    inp = generate(1, 2, 1024, 1024, 128, 64, seed=49, variant="icl", grad=True)
+    _, g1, _ = _fwd_bwd(inp, 1, 2, 1024, 1024, 128, 0.25, 0.5)
+    _, g2, _ = _fwd_bwd(inp, 1, 2, 1024, 1024, 128, 0.25, 0.5)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_workload_b2_n16384_sampled_heads():
+    c = CONFIGS[5]
+    B, H, L_src, L_ctx, D = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"]
+    _say(f"bwd workload {c['name']} seed {c['seed']}")
+    inp = generate_config(5)
+    plan, grads, aux = _fwd_bwd(inp, B, H, L_src, L_ctx, D, c["alpha_s"], c["alpha_f"])
+    got = [out_f64(g) for g in grads]
+    for g in got:
+        assert np.isfinite(g).all()
+    for bi, h in ((0, 3), (1, 29)):
+        sl = (slice(bi, bi + 1), slice(h, h + 1))
+        ref = orc.isa_ref_bwd(*(to_f64(inp[x][sl], "bf16") for x in ("q", "k", "v", "do")),
+                              L_src, L_ctx, 64, aux["sel"][sl], aux["flat"][sl])
+        _check_grads([g[sl] for g in got], ref, f"head ({bi},{h})")
