@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=3,
                     help="heads of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--bwd-config", type=int, default=5,
+                    help="workload of the backward measurement (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, launch a plain 256 MiB fp32 copy kernel (x2 scale) "
                          "whose FETCH_SIZE / WRITE_SIZE calibrate the HBM counters")
@@ -109,6 +112,53 @@ def summarize(paths):
                 v = np.array(v) / 1e3
                 print(f"{k:56s} {g:12d} {len(v):6d} {v.mean():10.1f} {v.min():10.1f} "
                       f"{v.max():10.1f}")
+
+
+def bench_backward(args, isa, torch, dev):
+    """Forward + decision-frozen backward on the backward workload."""
+    from synth import CONFIGS, generate_config
+
+    c = CONFIGS[args.bwd_config]
+    B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
+    N = L_src + L_ctx
+    _log(f"backward workload {c['name']}")
+    inp = generate_config(args.bwd_config)
+    to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, do = (to_gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    del inp
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"])
+    info = plan.info
+    o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
+    ws = torch.empty(max(isa._lib().isa_backward_workspace_bytes(plan.handle), 1),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        isa.isa_backward(plan, q, k, v, o, do, lse, aux, workspace=ws)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.bwd_steps):
+        isa.isa_backward(plan, q, k, v, o, do, lse, aux, workspace=ws)
+    s1.record()
+    torch.cuda.synchronize()
+    bms = s0.elapsed_time(s1) / args.bwd_steps
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.bwd_steps):
+        isa.isa_forward(plan, q, k, v, o, lse)
+    f1.record()
+    torch.cuda.synchronize()
+    fms = f0.elapsed_time(f1) / args.bwd_steps
+    # algorithmic backward work: 2.5x the forward's (5 matmuls per query-key pair)
+    exact_pairs = B * H * info["n_sharp"] * b * info["l_new"]
+    taylor_pairs = B * H * info["n_flat"] * b * info["n_kv_blocks"]
+    bwd_flops = 10.0 * D * (exact_pairs + taylor_pairs)
+    _log(f"backward {bms:.3f} ms, forward {fms:.3f} ms")
+    return {"workload": c["name"], "B": B, "H": H, "N": N, "alpha_s": c["alpha_s"],
+            "alpha_f": c["alpha_f"], "fwd_ms": fms, "bwd_ms": bms,
+            "bwd_algorithmic_tflop": bwd_flops / 1e12,
+            "bwd_tflops": bwd_flops / (bms * 1e-3) / 1e12,
+            "bwd_mfma_frac": bwd_flops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12}
 
 
 def main():
@@ -209,6 +259,10 @@ def main():
         "attn_taylor": {"ms": stage_ms["attn_taylor"],
                         "TFLOP/s": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12},
     }
+    backward = None
+    if args.bwd_config:
+        del o, lse, ws
+        backward = bench_backward(args, isa, torch, dev)
     cpu = None
     if args.cpu_heads > 0:
         _log(f"CPU oracle on {args.cpu_heads} heads")
@@ -227,6 +281,7 @@ def main():
         "dense_baseline": dense,
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
         "roofline": roofline,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

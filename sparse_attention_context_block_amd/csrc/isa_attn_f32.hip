@@ -5,6 +5,8 @@
 //
 // Workgroup = one 64-row query block; 4 threads per query row, each owning a
 // quarter of D.  Keys stream through LDS in 32-row tiles.
+#include <stdlib.h>
+
 #include "isa_internal.h"
 
 namespace isa {
@@ -74,12 +76,24 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
   if (p.lse && part == 0) p.lse[bh * p.lse_head_stride + qrow] = m + logf(l) + p.lse_offset;
 }
 
+// ISA_ATTN_4WAVE=1 selects the 4-wave kernel for every bf16 launch (comparison)
+bool force_4wave() {
+  static const bool f = [] {
+    const char* e = getenv("ISA_ATTN_4WAVE");
+    return e && e[0] == '1';
+  }();
+  return f;
+}
+
 }  // namespace
 
-hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
-
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream) {
-  if (dtype == ISA_DTYPE_BF16) return launch_attention_bf16(p, stream);
+  if (dtype == ISA_DTYPE_BF16) {
+    // whole 64-row key tiles (block table or contiguous keys): ping-pong kernel
+    const bool row_table = p.kv_tab && p.kv_row_shift == 0;
+    if (!row_table && p.kv_rows >= 64 && p.kv_rows % 64 == 0 && !force_4wave()) return launch_attention_pp(p, stream);
+    return launch_attention_bf16(p, stream);
+  }
   if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;
   dim3 grid(p.n_q_entries, p.BH);
   if (p.D == 128)

@@ -50,6 +50,11 @@ struct AttnParams {
 
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream);
 
+// bf16 kernels: the 4-wave kernel (any key source; used for row tables) and
+// the 8-wave ping-pong kernel (whole 64-row key tiles: exact path, dense).
+hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attention_pp(const AttnParams& p, hipStream_t stream);
+
 hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t dtype,
                        int BH, int N, int D, int L_src, int n_src, int n_q, int block,
                        double* qc, double* kc, void* kc_lp, void* vc_lp, hipStream_t stream);
