@@ -23,6 +23,14 @@ import time
 import numpy as np
 
 METRIC = "ISA fwd latency (ms) + dense-equiv TFLOP/s at N=32K,H=40,D=128 bf16"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM traffic of the exact-path kernel measured with rocprofv3 (FETCH_SIZE and
+# WRITE_SIZE, scaled by the same counters on a plain copy), with the SHA-256 of
+# the kernel source it was measured on; reported only while that source is
+# unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_exact_isa_bf16_N32768_hbm_traffic.txt")
+EXACT_KERNEL_SRC = os.path.join(ROOT, "sparse_attention_context_block_amd", "csrc",
+                                "isa_attn_pp.hip")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -76,6 +84,30 @@ def cpu_baseline(inp, c, n_heads):
             "latency_ms_extrapolated": per_job_s * 1e3,
             "sample": f"isa_ref (fp64 NumPy) on {n_heads} of {B * H} heads of the same input, "
                       f"{dt:.1f} s, extrapolated linearly to all heads"}
+
+
+def kernel_source_sha256():
+    import hashlib
+
+    return hashlib.sha256(open(EXACT_KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch from the committed counter summary, or None if the
+    kernel source changed since it was measured (or there is none)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != kernel_source_sha256():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _short(name):
@@ -161,9 +193,46 @@ def bench_backward(args, isa, torch, dev):
             "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12}
 
 
+def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_pp_kernel<128>"):
+    """Traffic file text: per-launch HBM bytes of `kernel`, from rocprofv3
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on
+    the 256 MiB copy of --calibrate-copy (268435456 bytes read and written)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            if _short(r["Kernel_Name"]) == kernel:
+                vals.append(float(r["Counter_Value"]))
+            elif "MulFunctor" in r["Kernel_Name"]:
+                copy.append(float(r["Counter_Value"]))
+        return float(np.mean(vals)), float(np.mean(copy))
+
+    known_kib = 268435456 / 1024.0
+    f, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    w, wc = per_kernel(write_csv, "WRITE_SIZE")
+    fs, ws = known_kib / fc, known_kib / wc
+    fetch_b, write_b = f * fs * 1024.0, w * ws * 1024.0
+    lines = [
+        f"# HBM traffic of {kernel} (exact path, ISA bf16 N=32768 H=40 D=128, alpha_s=0.25 alpha_f=0.5)",
+        f"# FETCH_SIZE {f:.1f} KiB/dispatch x copy scale {fs:.4f} (copy read {fc:.1f} KiB for 262144 KiB)",
+        f"# WRITE_SIZE {w:.1f} KiB/dispatch x copy scale {ws:.4f} (copy wrote {wc:.1f} KiB for 262144 KiB)",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"source_sha256: {kernel_source_sha256()}",
+    ]
+    return "\n".join(lines)
+
+
 def main():
     if len(sys.argv) > 2 and sys.argv[1] == "--summarize":
         summarize(sys.argv[2:])
+        return
+    if len(sys.argv) == 4 and sys.argv[1] == "--hbm-traffic":
+        print(hbm_traffic(sys.argv[2], sys.argv[3]))
         return
     args = parse()
     if args.gpus != 1:
@@ -245,9 +314,9 @@ def main():
     pool_bytes = 3.0 * B * H * N * D * 2 + B * H * info["n_q_blocks"] * D * (8 + 8 + 2 + 2)
     ex_ms = stage_ms["attn_exact"]
     achieved = exact_flops / (ex_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_fwd_bf16_kernel<128> (exact path)", "bound": "mfma",
+    roofline = {"kernel": "attn_fwd_pp_kernel<128> (exact path)", "bound": "mfma",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                 "algorithmic_flops_per_launch": exact_flops, "avg_launch_ms": ex_ms}
     stages = {
         "pool": {"ms": stage_ms["pool"], "GB/s": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9,
