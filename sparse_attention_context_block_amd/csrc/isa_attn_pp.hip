@@ -34,9 +34,7 @@ constexpr int kGroup = 256;  // threads per group
 constexpr int kBN = 64;      // keys per tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-// Workgroup barrier between phases.  The compiler may still move pure ALU
-// work across it (it has no memory dependence); letting it slide the tail of
-// the softmax into the MFMA phase measured faster than a hard fence.
+// Workgroup barrier between phases.
 __device__ __forceinline__ void phase_barrier() { __syncthreads(); }
 
 __device__ inline uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
@@ -284,7 +282,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
         if (t + 2 < n_tiles) load_v(ent);
       }
     }
+    // keep the exps of the softmax in this VALU phase: without the fences the
+    // scheduler moves them past the barrier into the MFMA phase
+    __builtin_amdgcn_sched_barrier(0);
     phase_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     pv(v_lds(t & 1));
     if (t + 1 < n_tiles) qk(k_lds((t + 1) & 1));
     // A: 2 barriers per tile; B skips the one after its last MFMA phase
