@@ -22,6 +22,11 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Per-source additions.  The backward kernels run one wave per SIMD, where the
+# compiler would otherwise place every MFMA accumulator in AGPRs and copy S, dP
+# and the staging registers between AGPRs and VGPRs on every key tile; the VGPR
+# form keeps the loops free of those copies.
+EXTRA = {"isa_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -42,7 +47,7 @@ def build(verbose=False, jobs=8):
     for src in sources:
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", src, "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for cmd, err in zip(cmds, ex.map(_run, cmds)):
             if verbose and err:
