@@ -37,6 +37,9 @@ from .isa_oracle import (  # noqa: F401
     gather_concat,
     exact_attention,
     taylor_attention,
+    ns_count,
+    top_ns_blocks,
+    mixed_attention,
     decisions_ref,
     isa_ref,
     isa_ref_fixed,

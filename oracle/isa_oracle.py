@@ -46,10 +46,23 @@ Readings of open points (each used identically by the HIP path):
   R13 Taylor path: per query row q (rows are not pooled),
       s_j = q . K^c_j / sqrt(D) over the n_src + k blocks of K_new,
       O = sum_j w_j e^{s_j - m} V^c_j / sum_j w_j e^{s_j - m}.
-  R14 no exact blocks inside a flat row (no-sparsity ratio alpha_ns = 0).
+  R14 by default no exact blocks inside a flat row (no-sparsity ratio
+      alpha_ns = 0); R21 gives the gating for alpha_ns > 0.
   R15 each row comes from one path; LSE = m + ln l (natural log).
   R16 no mask.  R17 max subtraction applied.
   R20 (backward) the decisions are constants; see ``isa_oracle_bwd``.
+  R21 block mask inside flat query blocks ([notes] key design 2: a block pair
+      with mask 1 takes the exact online-softmax update, mask 0 the
+      representative update; [summary] 2 "Pooling Attention": the mask comes
+      from the top entries of the coarse map; alpha_ns is the no-sparsity
+      ratio).  For flat query block i, rank the N_K' blocks of K_new by
+      S_coarse[i, j] (the full coarse row of R3, restricted to the kept
+      blocks), order key (S_coarse descending, position in K_new ascending),
+      and compute the first n_ns = ceil(alpha_ns * N_K') (1e-6 guard, clamped
+      to [0, N_K']) token by token; every other block of K_new enters through
+      its representative with weight w_j.  Both kinds of terms share one
+      softmax per row: l = sum_t e^{s_t - m} + sum_j w_j e^{s^c_j - m}.
+      Sharp query blocks are unchanged.
 """
 
 import math
@@ -184,6 +197,49 @@ def taylor_attention(Qrows, Kc_new, Vc_new, w_new):
     return O, m[:, 0] + np.log(l)
 
 
+# --------------------------------------------------------------------------
+# Block mask inside flat query blocks.  [notes] key design 2 (per block pair:
+# exact update when the mask is 1, representative update otherwise) and
+# [notes] key design 3 / [summary] 4 "Hyperparameters in ISA" (alpha_ns, the
+# no-sparsity ratio).  Reading R21.
+# --------------------------------------------------------------------------
+def ns_count(alpha_ns, n_kv):
+    """n_ns = ceil(alpha_ns * N_K') clamped to [0, N_K'] (R21)."""
+    n = math.ceil(alpha_ns * n_kv - _GUARD)
+    return int(min(max(n, 0), n_kv))
+
+
+def top_ns_blocks(p_row, n_ns):
+    """Positions (in K_new) of the n_ns largest coarse probabilities of a
+    query block, ties to the smaller position, returned ascending."""
+    u = np.arange(len(p_row))
+    order = np.lexsort((u, -np.asarray(p_row)))  # primary key: -p, then u
+    return np.sort(order[:n_ns]).astype(np.int64)
+
+
+def mixed_attention(Qrows, K_new, V_new, Kc_new, Vc_new, w_new, exact_blocks):
+    """Flat-row attention with a block mask (R21): the tokens of the K_new
+    blocks in ``exact_blocks`` (positions) enter one by one, every other
+    block through K^c_j, V^c_j with weight w_j; one softmax over both."""
+    w = np.asarray(w_new, dtype=np.float64)
+    ends = np.cumsum(w).astype(np.int64)
+    starts = ends - w.astype(np.int64)
+    exact = np.zeros(len(w), dtype=bool)
+    exact[np.asarray(exact_blocks, dtype=np.int64)] = True
+    tok = (np.concatenate([np.arange(starts[u], ends[u]) for u in np.nonzero(exact)[0]])
+           if exact.any() else np.zeros(0, dtype=np.int64))
+    rep = np.nonzero(~exact)[0]
+    D = Qrows.shape[1]
+    S_tok = (Qrows @ K_new[tok].T) / math.sqrt(D)
+    S_rep = (Qrows @ Kc_new[rep].T) / math.sqrt(D)
+    m = np.concatenate([S_tok, S_rep], axis=1).max(axis=1, keepdims=True)
+    E_tok = np.exp(S_tok - m)
+    E_rep = np.exp(S_rep - m) * w[rep][None, :]
+    l = E_tok.sum(axis=1) + E_rep.sum(axis=1)
+    O = (E_tok @ V_new[tok] + E_rep @ Vc_new[rep]) / l[:, None]
+    return O, m[:, 0] + np.log(l)
+
+
 def _rows_of_blocks(blocks, starts, ends):
     if len(blocks) == 0:
         return np.zeros(0, dtype=np.int64)
@@ -199,7 +255,7 @@ def _chunks(rows, size=2048):
         yield rows[s:s + size]
 
 
-def _head_decisions(Qh, Kh, L_src, L_ctx, b, alpha_s, alpha_f):
+def _head_decisions(Qh, Kh, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns=0.0):
     starts, ends, n_src, n_ctx = block_grid(L_src, L_ctx, b)
     Qc = pool_blocks(Qh, starts, ends)
     Kc = pool_blocks(Kh, starts, ends)
@@ -208,11 +264,18 @@ def _head_decisions(Qh, Kh, L_src, L_ctx, b, alpha_s, alpha_f):
     sel = top_k_context(c, select_count(alpha_s, n_ctx))
     M = sharpness(P)
     flat, sharp = route_queries(M, flat_count(alpha_f, len(starts)))
-    return dict(c=c, M=M, sel=sel, flat=flat, sharp=sharp)
+    kept = np.concatenate([np.arange(n_src), n_src + sel]).astype(np.int64)
+    n_ns = ns_count(alpha_ns, len(kept))
+    ns = np.stack([top_ns_blocks(P[i, kept], n_ns) for i in flat]) if len(flat) \
+        else np.zeros((0, n_ns), dtype=np.int64)
+    return dict(c=c, M=M, sel=sel, flat=flat, sharp=sharp, ns=ns.reshape(len(flat), n_ns))
 
 
-def _head_paths(Qh, Kh, Vh, L_src, L_ctx, b, sel, flat, rows=None):
-    """Steps 3 (gather) and 5-7 for one head with fixed decisions."""
+def _head_paths(Qh, Kh, Vh, L_src, L_ctx, b, sel, flat, rows=None, ns=None):
+    """Steps 3 (gather) and 5-7 for one head with fixed decisions.
+
+    ``ns`` [n_flat, n_ns] (optional, R21): per flat block (in the order of
+    ``flat``) the K_new positions computed exactly."""
     starts, ends, n_src, n_ctx = block_grid(L_src, L_ctx, b)
     n_q = len(starts)
     K_new = gather_concat(Kh, starts, ends, n_src, sel)
@@ -232,43 +295,50 @@ def _head_paths(Qh, Kh, Vh, L_src, L_ctx, b, sel, flat, rows=None):
     O = np.zeros((len(rows), Vh.shape[1]))
     lse = np.zeros(len(rows))
     flat_mask = is_flat[block_of_row[rows]]
-    for mask, path in ((~flat_mask, "exact"), (flat_mask, "taylor")):
-        pos = np.nonzero(mask)[0]
-        for chunk in _chunks(pos):
-            q = Qh[rows[chunk]]
-            if path == "exact":
-                o, l = exact_attention(q, K_new, V_new)
-            else:
-                o, l = taylor_attention(q, Kc_new, Vc_new, w_new)
-            O[chunk], lse[chunk] = o, l
+    for pos in _chunks(np.nonzero(~flat_mask)[0]):
+        O[pos], lse[pos] = exact_attention(Qh[rows[pos]], K_new, V_new)
+    if ns is None or np.asarray(ns).size == 0:
+        for pos in _chunks(np.nonzero(flat_mask)[0]):
+            O[pos], lse[pos] = taylor_attention(Qh[rows[pos]], Kc_new, Vc_new, w_new)
+    else:
+        flat = np.asarray(flat, dtype=np.int64)
+        for f, i in enumerate(flat):
+            pos = np.nonzero(block_of_row[rows] == i)[0]
+            if len(pos):
+                O[pos], lse[pos] = mixed_attention(Qh[rows[pos]], K_new, V_new, Kc_new, Vc_new,
+                                                   w_new, ns[f])
     return O, lse
 
 
-def decisions_ref(Q, K, L_src, L_ctx, b, alpha_s, alpha_f):
+def decisions_ref(Q, K, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns=0.0):
     """Steps 1-4 for every (batch, head).
 
     Returns dict of arrays indexed [B, H, ...]: c (context scores), M
-    (sharpness), sel (selected context blocks), flat and sharp (query blocks).
-    k and n_flat depend only on the shapes, so every head has the same sizes.
+    (sharpness), sel (selected context blocks), flat and sharp (query blocks),
+    ns (R21: per flat block the K_new positions computed exactly, [.., n_flat,
+    n_ns]).  k, n_flat and n_ns depend only on the shapes, so every head has
+    the same sizes.
     """
     Q, K = _f64(Q), _f64(K)
     B, H = Q.shape[:2]
-    per_head = [_head_decisions(Q[bi, h], K[bi, h], L_src, L_ctx, b, alpha_s, alpha_f)
+    per_head = [_head_decisions(Q[bi, h], K[bi, h], L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns)
                 for bi in range(B) for h in range(H)]
     out = {}
-    for key in ("c", "M", "sel", "flat", "sharp"):
+    for key in ("c", "M", "sel", "flat", "sharp", "ns"):
         arr = np.stack([d[key] for d in per_head]) if per_head else np.zeros((0, 0))
         out[key] = arr.reshape((B, H) + arr.shape[1:])
     return out
 
 
-def isa_ref_fixed(Q, K, V, L_src, L_ctx, b, sel, flat, rows=None):
+def isa_ref_fixed(Q, K, V, L_src, L_ctx, b, sel, flat, rows=None, ns=None):
     """Steps 3 (gather) and 5-7 with the decisions supplied.
 
     sel [B, H, k] and flat [B, H, n_flat] are the selected context blocks and
-    the flat query blocks of every head.  ``rows`` (optional) restricts the
-    output to those token rows of every head; each row is computed exactly as
-    in the full evaluation.  Returns (O [B,H,R,D], LSE [B,H,R]).
+    the flat query blocks of every head; ns [B, H, n_flat, n_ns] (optional,
+    R21) the exact K_new blocks of every flat block.  ``rows`` (optional)
+    restricts the output to those token rows of every head; each row is
+    computed exactly as in the full evaluation.  Returns (O [B,H,R,D],
+    LSE [B,H,R]).
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, D = Q.shape
@@ -278,16 +348,16 @@ def isa_ref_fixed(Q, K, V, L_src, L_ctx, b, sel, flat, rows=None):
     for bi in range(B):
         for h in range(H):
             O[bi, h], LSE[bi, h] = _head_paths(Q[bi, h], K[bi, h], V[bi, h], L_src, L_ctx, b,
-                                               sel[bi][h], flat[bi][h], rows)
+                                               sel[bi][h], flat[bi][h], rows,
+                                               None if ns is None else ns[bi][h])
     return O, LSE
 
 
 def isa_ref(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns=0.0):
-    """The whole ISA forward: dict(O, LSE, c, M, sel, flat, sharp), [B, H, ...]."""
-    if alpha_ns != 0.0:
-        raise NotImplementedError("alpha_ns > 0 (exact blocks inside flat rows) is not defined here")
-    dec = decisions_ref(Q, K, L_src, L_ctx, b, alpha_s, alpha_f)
-    O, LSE = isa_ref_fixed(Q, K, V, L_src, L_ctx, b, dec["sel"], dec["flat"])
+    """The whole ISA forward: dict(O, LSE, c, M, sel, flat, sharp, ns), [B, H, ...]."""
+    dec = decisions_ref(Q, K, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns)
+    O, LSE = isa_ref_fixed(Q, K, V, L_src, L_ctx, b, dec["sel"], dec["flat"],
+                           ns=dec["ns"] if alpha_ns > 0 else None)
     out = dict(O=O, LSE=LSE)
     out.update(dec)
     return out

@@ -40,6 +40,17 @@ MUTATIONS = [
      "Kc_new = pool_blocks(Kh, starts, ends)[:len(kept)]"),
     ("flat takes the largest M", "flat = np.sort(order[:n_flat]).astype(np.int64)",
      "flat = np.sort(order[-n_flat:] if n_flat else order[:0]).astype(np.int64)"),
+    ("masked blocks also enter the Taylor sum", "rep = np.nonzero(~exact)[0]",
+     "rep = np.arange(len(w))"),
+    ("exact tokens weighted by the block length", "E_tok = np.exp(S_tok - m)\n",
+     "E_tok = np.exp(S_tok - m) * w[0]\n"),
+    ("mask keeps the smallest coarse scores", "order = np.lexsort((u, -np.asarray(p_row)))",
+     "order = np.lexsort((u, np.asarray(p_row)))"),
+    ("mask ranks the first blocks, not the kept ones", "top_ns_blocks(P[i, kept], n_ns)",
+     "top_ns_blocks(P[i, :len(kept)], n_ns)"),
+    ("mask count floors", "n = math.ceil(alpha_ns * n_kv - _GUARD)", "n = math.floor(alpha_ns * n_kv)"),
+    ("mixed drops the representative weight", "E_rep = np.exp(S_rep - m) * w[rep][None, :]",
+     "E_rep = np.exp(S_rep - m)"),
 ]
 
 
@@ -53,6 +64,7 @@ def test_pins_reject_planted_mistake(tmp_path, name, old, new):
     shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
     (tmp_path / "oracle" / "isa_oracle.py").write_text(src.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py",
+                        "tests/test_oracle_ns_pins.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"no pin caught the planted mistake: {name}\n{r.stdout[-2000:]}"
