@@ -26,8 +26,8 @@
  *   - Argument errors are detected on the host before the first launch, so
  *     on error nothing has been written.  No entry point aborts or throws.
  *   - Supported on the device: block = 64, D in {64, 128}, L_src and L_ctx
- *     multiples of 64, alpha_ns = 0, dtype BF16 (fp32 accumulation) or FP32.
- *     Other valid descriptions return ISA_ERR_UNSUPPORTED.
+ *     multiples of 64, dtype BF16 (fp32 accumulation) or FP32.  Other valid
+ *     descriptions return ISA_ERR_UNSUPPORTED.
  */
 #ifndef ISA_H
 #define ISA_H
@@ -58,7 +58,9 @@ typedef struct {
   double alpha_s;        /* select ratio: keep ceil(alpha_s * n_ctx) context blocks   */
   double alpha_f;        /* flat ratio: floor(alpha_f * n_q) flattest query blocks go */
                          /* to the 0-th order Taylor path ([notes] key design 3)      */
-  double alpha_ns;       /* no-sparsity ratio inside flat rows; must be 0             */
+  double alpha_ns;       /* no-sparsity ratio: inside each flat query block the        */
+                         /* ceil(alpha_ns * n_kv) K_new blocks with the largest coarse */
+                         /* score are computed exactly ([notes] key design 2 mask)    */
   isa_dtype_t dtype;     /* storage and input type of Q, K, V, O                      */
 } isa_plan_desc_t;
 
@@ -75,6 +77,8 @@ typedef struct {
   int64_t n_flat;         /* query blocks on the Taylor path, floor(alpha_f * n_q) */
   int64_t n_sharp;        /* query blocks on the exact path, n_q - n_flat */
   size_t workspace_bytes; /* device workspace isa_forward needs */
+  int64_t n_ns;           /* K_new blocks computed exactly per flat query block, */
+                          /* ceil(alpha_ns * n_kv) (0: the plain Taylor path)     */
 } isa_plan_info_t;
 
 /* Optional device outputs of isa_forward (each pointer may be NULL). */
@@ -85,6 +89,10 @@ typedef struct {
   double* ctx_score;   /* [B, H, n_ctx]   c_j, the source-query mean of the coarse   */
                        /*                 map over context block j                   */
   double* sharpness;   /* [B, H, n_q]     M_i, the variance of coarse row i          */
+  int32_t* ns;         /* [B, H, n_flat, n_ns] per flat query block (in the order of */
+                       /*                 flat) the positions in K_new (0..n_kv-1:   */
+                       /*                 source blocks, then the kept context       */
+                       /*                 blocks) computed exactly, ascending        */
 } isa_aux_t;
 
 /* Validate a description and derive the sizes; host only, never calls HIP.
@@ -92,7 +100,7 @@ typedef struct {
  * Errors: ISA_ERR_INVALID_ARG (null out/desc, B/H/D/block < 1 or negative,
  * L_src < 1, L_ctx < 0, a ratio outside [0, 1] or NaN),
  * ISA_ERR_UNSUPPORTED (block != 64, D not 64/128, L_src or L_ctx not a
- * multiple of 64, alpha_ns != 0, unknown dtype). */
+ * multiple of 64, unknown dtype). */
 isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc);
 
 /* Copy the derived sizes into *info.  Host only. */
@@ -111,7 +119,10 @@ isa_status_t isa_plan_destroy(isa_plan_t plan);
  *      the smallest M_i (ties to the smaller i) are flat;
  *   4. sharp rows: exact softmax(q K_new^T / sqrt(D)) V_new; flat rows:
  *      0-th order Taylor attention against the block means of K_new, V_new
- *      with block-length weights ([notes] key design 2);
+ *      with block-length weights ([notes] key design 2).  With n_ns > 0 the
+ *      n_ns K_new blocks of largest coarse score x_ij of flat block i (ties
+ *      to the smaller K_new position) enter token by token instead, in the
+ *      same softmax;
  *   5. O = O / l (bf16 round-to-nearest-even for BF16), lse = m + ln l.
  * Q, K, V, O: [B, H, N, D] of `dtype`.  lse: [B, H, N] float, may be NULL.
  * aux: optional decision outputs (see isa_aux_t), may be NULL.
@@ -165,8 +176,8 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * selected receive zero.  Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D]; lse:
  * [B, H, N] float from the forward; aux: sel, flat and sharp from the
  * forward (required).  workspace: at least isa_backward_workspace_bytes().
- * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32), ISA_ERR_WORKSPACE,
- * ISA_ERR_HIP. */
+ * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, or a plan with
+ * n_ns > 0), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

@@ -51,12 +51,13 @@ class isa_plan_info_t(ctypes.Structure):
                 ("n_q_blocks", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("n_kv_blocks", ctypes.c_int64), ("l_new", ctypes.c_int64),
                 ("n_flat", ctypes.c_int64), ("n_sharp", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("n_ns", ctypes.c_int64)]
 
 
 class isa_aux_t(ctypes.Structure):
     _fields_ = [("sel", ctypes.c_void_p), ("flat", ctypes.c_void_p), ("sharp", ctypes.c_void_p),
-                ("ctx_score", ctypes.c_void_p), ("sharpness", ctypes.c_void_p)]
+                ("ctx_score", ctypes.c_void_p), ("sharpness", ctypes.c_void_p),
+                ("ns", ctypes.c_void_p)]
 
 
 _L = None
@@ -156,8 +157,9 @@ def isa_forward(plan, q, k, v, o=None, lse=None, aux=False, workspace=None, stre
                 events=None):
     """Run the ISA forward.  Returns (o, lse, aux_dict or None).
 
-    ``aux=True`` also returns the decisions: sel, flat, sharp (int32) and
-    ctx_score, sharpness (float64), each [B, H, ...].  ``events``: optional
+    ``aux=True`` also returns the decisions: sel, flat, sharp (int32),
+    ctx_score, sharpness (float64), each [B, H, ...], and with a block mask
+    (info n_ns > 0) ns [B, H, n_flat, n_ns] (int32).  ``events``: optional
     list of ISA_PROFILE_STAGES + 1 torch.cuda.Event(enable_timing=True),
     recorded before the first stage and after every stage
     (isa_forward_profiled).
@@ -182,6 +184,9 @@ def isa_forward(plan, q, k, v, o=None, lse=None, aux=False, workspace=None, stre
             sharp=torch.empty(bh + (info["n_sharp"],), dtype=torch.int32, device=dev),
             ctx_score=torch.empty(bh + (info["n_ctx_blocks"],), dtype=torch.float64, device=dev),
             sharpness=torch.empty(bh + (info["n_q_blocks"],), dtype=torch.float64, device=dev))
+        if info["n_ns"] > 0 and info["n_flat"] > 0:
+            out_aux["ns"] = torch.empty(bh + (info["n_flat"], info["n_ns"]), dtype=torch.int32,
+                                        device=dev)
         for f, t in out_aux.items():
             setattr(a, f, t.data_ptr() if t.numel() else None)
     if workspace is None:

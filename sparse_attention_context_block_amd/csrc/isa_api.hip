@@ -13,6 +13,7 @@ using namespace isa;
 
 struct WorkspaceLayout {
   size_t qc, kc, kc_lp, vc_lp, rowmax, rowsum, sharpness, ctx_score, sel, flat, sharp, kv_tab;
+  size_t logits, ns;  // only with n_ns > 0 and n_flat > 0
   size_t total;
 };
 
@@ -57,6 +58,11 @@ int64_t flat_count(double alpha_f, int64_t n_q) {
   int64_t n = (int64_t)floor(alpha_f * (double)n_q + 1e-6);
   return n < 0 ? 0 : (n > n_q ? n_q : n);
 }
+// K_new blocks computed exactly per flat query block: ceil(alpha_ns * n_kv).
+int64_t ns_count(double alpha_ns, int64_t n_kv) {
+  int64_t n = (int64_t)ceil(alpha_ns * (double)n_kv - 1e-6);
+  return n < 0 ? 0 : (n > n_kv ? n_kv : n);
+}
 
 bool ratio_ok(double a) { return a >= 0.0 && a <= 1.0; }  // false for NaN
 
@@ -89,7 +95,6 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   if ((int64_t)d.L_src + d.L_ctx > INT32_MAX / 2) return ISA_ERR_UNSUPPORTED;
   if (d.block != kBlock || (d.D != 64 && d.D != 128)) return ISA_ERR_UNSUPPORTED;
   if (d.L_src % kBlock != 0 || d.L_ctx % kBlock != 0) return ISA_ERR_UNSUPPORTED;
-  if (d.alpha_ns != 0.0) return ISA_ERR_UNSUPPORTED;
   const int64_t BH = (int64_t)d.B * d.H;
   if (BH > 65535) return ISA_ERR_UNSUPPORTED;
 
@@ -112,6 +117,7 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   in.l_new = (int64_t)d.L_src + in.k * d.block;
   in.n_flat = flat_count(d.alpha_f, in.n_q_blocks);
   in.n_sharp = in.n_q_blocks - in.n_flat;
+  in.n_ns = ns_count(d.alpha_ns, in.n_kv_blocks);
 
   WorkspaceLayout& w = p->ws;
   size_t off = 0;
@@ -133,6 +139,9 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   w.flat = take((size_t)BH * in.n_flat * sizeof(int32_t));
   w.sharp = take((size_t)BH * in.n_sharp * sizeof(int32_t));
   w.kv_tab = take((size_t)BH * in.n_kv_blocks * sizeof(int32_t));
+  const bool masked = in.n_ns > 0 && in.n_flat > 0;
+  w.logits = masked ? take((size_t)BH * in.n_q_blocks * in.n_q_blocks * sizeof(double)) : 0;
+  w.ns = masked ? take((size_t)BH * in.n_flat * in.n_ns * sizeof(int32_t)) : 0;
   w.total = off;
   in.workspace_bytes = off;
   *out = p;
@@ -187,6 +196,10 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   int32_t* flat = (aux && aux->flat) ? aux->flat : reinterpret_cast<int32_t*>(w + L.flat);
   int32_t* sharp = (aux && aux->sharp) ? aux->sharp : reinterpret_cast<int32_t*>(w + L.sharp);
   int32_t* kv_tab = reinterpret_cast<int32_t*>(w + L.kv_tab);
+  const bool masked = in.n_ns > 0 && in.n_flat > 0;
+  double* logits = masked ? reinterpret_cast<double*>(w + L.logits) : nullptr;
+  int32_t* ns = !masked ? nullptr
+                        : (aux && aux->ns) ? aux->ns : reinterpret_cast<int32_t*>(w + L.ns);
   const int BH = plan->BH, D = d.D, N = (int)plan->N;
   const int n_q = (int)in.n_q_blocks, n_src = (int)in.n_src_blocks, n_ctx = (int)in.n_ctx_blocks;
 
@@ -201,7 +214,7 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   ISA_LAUNCH(launch_pool(Q, K, V, d.dtype, BH, N, D, d.L_src, n_src, n_q, d.block, qc, kc,
                          kc_lp, vc_lp, s));
   ISA_STAGE(1);
-  ISA_LAUNCH(launch_coarse_rowstats(qc, kc, BH, n_q, D, rowmax, rowsum, sharpness, s));
+  ISA_LAUNCH(launch_coarse_rowstats(qc, kc, BH, n_q, D, rowmax, rowsum, sharpness, logits, s));
   ISA_STAGE(2);
   ISA_LAUNCH(launch_coarse_colsum(qc, kc, rowmax, rowsum, BH, n_q, n_src, n_ctx, D, ctx_score,
                                   s));
@@ -209,6 +222,10 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   // 2-3. TopK of the context blocks (block table of K_new) and routing
   ISA_LAUNCH(launch_select_route(ctx_score, sharpness, BH, n_src, n_ctx, n_q, (int)in.k,
                                  (int)in.n_flat, sel, flat, sharp, kv_tab, s));
+  //    block mask of the flat query blocks: their top n_ns blocks of K_new
+  if (masked)
+    ISA_LAUNCH(launch_ns_select(logits, flat, kv_tab, BH, n_q, (int)in.n_flat,
+                                (int)in.n_kv_blocks, (int)in.n_ns, ns, s));
   ISA_STAGE(4);
 
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -238,7 +255,37 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   ISA_STAGE(5);
 
   // 4b. 0-th order Taylor path: flat query blocks over the block means of the
-  //     K_new blocks; every block holds b tokens, weight b
+  //     K_new blocks; every block holds b tokens, weight b.  With the block
+  //     mask, each flat block's n_ns blocks enter token by token instead.
+  if (masked) {
+    FlatParams pf;
+    memset(&pf, 0, sizeof(pf));
+    pf.q = Q;
+    pf.k = K;
+    pf.v = V;
+    pf.kc = kc_lp;
+    pf.vc = vc_lp;
+    pf.o = O;
+    pf.lse = lse;
+    pf.flat = flat;
+    pf.kv_tab = kv_tab;
+    pf.ns = ns;
+    pf.n_flat = (int)in.n_flat;
+    pf.n_kv = (int)in.n_kv_blocks;
+    pf.n_ns = (int)in.n_ns;
+    pf.q_head_stride = plan->N * D;
+    pf.kv_head_stride = plan->N * D;
+    pf.kc_head_stride = (int64_t)n_q * D;
+    pf.lse_head_stride = plan->N;
+    pf.BH = BH;
+    pf.D = D;
+    pf.scale_log2 = scale_log2;
+    pf.exact_bias_log2 = (float)(-log2((double)d.block));
+    pf.lse_offset = (float)log((double)d.block);
+    ISA_LAUNCH(launch_attention_flat(pf, d.dtype, s));
+    ISA_STAGE(6);
+    return ISA_OK;
+  }
   AttnParams pt = pe;
   pt.k = kc_lp;
   pt.v = vc_lp;
@@ -367,6 +414,7 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   for (const void* q : ptrs)
     if (!aligned16(q)) return ISA_ERR_INVALID_ARG;
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
+  if (plan->info.n_ns > 0 && plan->info.n_flat > 0) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);

@@ -10,6 +10,8 @@
 //             M_i = (N_K q_i - l_i^2) / (N_K^2 l_i^2).  In fp64 this has a
 //             relative error of about 1e-11 at N_K = 800, far below any gap the
 //             routing compares, and it is exactly 0 for a uniform row.
+//             With alpha_ns > 0 it also stores every x_ij (fp64), which the
+//             block mask of the flat query blocks ranks.
 //   colsum:   per context block j, c_j = mean over source query blocks i of
 //             S_coarse[i, n_src + j] ([notes] key design 1), reduced in a fixed
 //             order (no atomics), so the result is deterministic.
@@ -59,7 +61,8 @@ __device__ inline void tile_dot(const double (*QT)[kT], const double (*KT)[kT], 
 template <int D>
 __global__ __launch_bounds__(kThreads) void rowstats_kernel(
     const double* __restrict__ qc, const double* __restrict__ kc, int n_q, double scale,
-    double* __restrict__ rowmax, double* __restrict__ rowsum, double* __restrict__ sharpness) {
+    double* __restrict__ rowmax, double* __restrict__ rowsum, double* __restrict__ sharpness,
+    double* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) double QT[D][kT];
   __shared__ __attribute__((aligned(16))) double KT[D][kT];
   const int64_t bh = blockIdx.y;
@@ -83,6 +86,8 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const double x = acc[a][b] * scale;
+        if (logits && r0 + 2 * tr + a < n_q)
+          logits[(bh * n_q + r0 + 2 * tr + a) * (int64_t)n_q + c0 + 2 * tc + b] = x;
         if (x > m[a]) {
           const double f = exp(m[a] - x);  // 0 when m is -inf
           l[a] *= f;
@@ -182,16 +187,16 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(
 
 hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
                                   double* rowmax, double* rowsum, double* sharpness,
-                                  hipStream_t stream) {
+                                  double* logits, hipStream_t stream) {
   if (BH == 0 || n_q == 0) return hipSuccess;
   dim3 grid((n_q + kT - 1) / kT, BH);
   const double scale = 1.0 / sqrt((double)D);
   if (D == 128)
     hipLaunchKernelGGL(rowstats_kernel<128>, grid, dim3(kThreads), 0, stream, qc, kc, n_q, scale,
-                       rowmax, rowsum, sharpness);
+                       rowmax, rowsum, sharpness, logits);
   else
     hipLaunchKernelGGL(rowstats_kernel<64>, grid, dim3(kThreads), 0, stream, qc, kc, n_q, scale,
-                       rowmax, rowsum, sharpness);
+                       rowmax, rowsum, sharpness, logits);
   return hipGetLastError();
 }
 

@@ -55,13 +55,42 @@ hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t 
 hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attention_pp(const AttnParams& p, hipStream_t stream);
 
+// Flat query blocks with a block mask (alpha_ns > 0): per flat block, the
+// K_new blocks listed in ns token by token, every other block of K_new through
+// its pooled row.
+struct FlatParams {
+  const void* q;            // token rows [BH][N][D]
+  const void* k;
+  const void* v;
+  const void* kc;           // pooled rows [BH][n_q][D], same dtype
+  const void* vc;
+  void* o;
+  float* lse;
+  const int32_t* flat;      // [BH][n_flat] flat query blocks
+  const int32_t* kv_tab;    // [BH][n_kv] block ids of K_new
+  const int32_t* ns;        // [BH][n_flat][n_ns] K_new positions computed exactly
+  int32_t n_flat, n_kv, n_ns;
+  int64_t q_head_stride;    // N * D (Q, O)
+  int64_t kv_head_stride;   // N * D (K, V)
+  int64_t kc_head_stride;   // n_q * D (K^c, V^c)
+  int64_t lse_head_stride;  // N
+  int32_t BH, D;
+  float scale_log2;         // log2(e) / sqrt(D)
+  float exact_bias_log2;    // -log2(b): exact tokens weigh 1 against b per block
+  float lse_offset;         // ln(b)
+};
+hipError_t launch_attention_flat(const FlatParams& p, isa_dtype_t dtype, hipStream_t stream);
+hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int32_t* kv_tab,
+                            int BH, int n_q, int n_flat, int n_kv, int n_ns, int32_t* ns,
+                            hipStream_t stream);
+
 hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t dtype,
                        int BH, int N, int D, int L_src, int n_src, int n_q, int block,
                        double* qc, double* kc, void* kc_lp, void* vc_lp, hipStream_t stream);
 
 hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
                                   double* rowmax, double* rowsum, double* sharpness,
-                                  hipStream_t stream);
+                                  double* logits, hipStream_t stream);
 
 hipError_t launch_coarse_colsum(const double* qc, const double* kc, const double* rowmax,
                                 const double* rowsum, int BH, int n_q, int n_src, int n_ctx,

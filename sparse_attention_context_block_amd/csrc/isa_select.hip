@@ -107,7 +107,53 @@ __global__ __launch_bounds__(kThreads) void select_route_kernel(
   compact(flag, n_q, flat + bh * n_flat, sharp + bh * (int64_t)(n_q - n_flat), counts);
 }
 
+// Block mask of one flat query block i ([notes] key design 2; the mask is
+// read off the coarse map, [summary] 2 "Pooling Attention"): rank the n_kv
+// blocks of K_new by x_i,kv_tab[u] (descending; the coarse probability is
+// increasing in x), ties to the smaller position u, and keep the first n_ns,
+// listed ascending.  One workgroup per (flat entry, head).
+__global__ __launch_bounds__(kThreads) void ns_select_kernel(
+    const double* __restrict__ logits, const int32_t* __restrict__ flat,
+    const int32_t* __restrict__ kv_tab, int n_q, int n_flat, int n_kv, int n_ns,
+    int32_t* __restrict__ ns) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem);                // [n_kv]
+  uint8_t* flag = smem + sizeof(uint64_t) * kMaxBlocksPerHead;      // [n_kv]
+  int32_t* counts = reinterpret_cast<int32_t*>(flag + kMaxBlocksPerHead);  // [kThreads]
+  const int f = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int i = flat[bh * n_flat + f];
+  const double* row = logits + (bh * n_q + i) * (int64_t)n_q;
+  const int32_t* tab = kv_tab + bh * n_kv;
+  for (int u = tid; u < n_kv; u += kThreads) key[u] = order_key(row[tab[u]]);
+  __syncthreads();
+  for (int u = tid; u < n_kv; u += kThreads) {
+    const uint64_t ku = key[u];
+    int rank = 0;
+    for (int v = 0; v < n_kv; ++v) {
+      const uint64_t kv = key[v];
+      rank += (kv > ku || (kv == ku && v < u)) ? 1 : 0;
+    }
+    flag[u] = rank < n_ns ? 1 : 0;
+  }
+  __syncthreads();
+  compact(flag, n_kv, ns + (bh * n_flat + f) * (int64_t)n_ns, nullptr, counts);
+}
+
 }  // namespace
+
+hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int32_t* kv_tab,
+                            int BH, int n_q, int n_flat, int n_kv, int n_ns, int32_t* ns,
+                            hipStream_t stream) {
+  if (BH == 0 || n_flat == 0 || n_ns == 0) return hipSuccess;
+  if (n_kv < 1 || n_kv > kMaxBlocksPerHead || n_ns > n_kv) return hipErrorInvalidValue;
+  const size_t lds = sizeof(uint64_t) * kMaxBlocksPerHead + kMaxBlocksPerHead +
+                     sizeof(int32_t) * kThreads;
+  hipLaunchKernelGGL(ns_select_kernel, dim3(n_flat, BH), dim3(kThreads), lds, stream, logits,
+                     flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
+  return hipGetLastError();
+}
 
 hipError_t launch_select_route(const double* ctx_score, const double* sharpness, int BH,
                                int n_src, int n_ctx, int n_q, int k, int n_flat, int32_t* sel,

@@ -81,6 +81,22 @@ def check_routing(flat_gpu, sharp_gpu, M_ref, n_flat):
     return len(diff)
 
 
+def check_ns(ns_gpu, p_kept, n_ns):
+    """One flat block's exact K_new positions vs the oracle's top n_ns of its
+    coarse probabilities over the kept blocks (R21); returns the exemptions."""
+    p_kept = np.asarray(p_kept)
+    u = np.arange(len(p_kept))
+    order = np.lexsort((u, -p_kept))
+    want = set(order[:n_ns].tolist())
+    got = set(np.asarray(ns_gpu).tolist())
+    assert len(got) == n_ns and list(np.asarray(ns_gpu)) == sorted(got), "ns not ascending/unique"
+    diff = want ^ got
+    exempt = _band_exempt(p_kept, order, n_ns)
+    bad = [x for x in diff if not exempt[x]]
+    assert not bad, f"block mask differs outside the band at K_new positions {sorted(bad)}"
+    return len(diff)
+
+
 def check_close(got, ref, max_abs, mean_abs, what=""):
     err = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
     mx, mn = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0

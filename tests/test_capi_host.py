@@ -86,7 +86,7 @@ def test_plan_counts_follow_the_rounding_rule(alpha_s, alpha_f):
     (dict(D=96), isa.ISA_ERR_UNSUPPORTED),
     (dict(L_src=100), isa.ISA_ERR_UNSUPPORTED),
     (dict(L_ctx=70), isa.ISA_ERR_UNSUPPORTED),
-    (dict(alpha_ns=0.0625), isa.ISA_ERR_UNSUPPORTED),
+    (dict(alpha_ns=1.5), isa.ISA_ERR_INVALID_ARG),
     (dict(L_src=64 * 4097, L_ctx=0), isa.ISA_ERR_UNSUPPORTED),
 ])
 def test_plan_validation(kw, status):
@@ -95,6 +95,34 @@ def test_plan_validation(kw, status):
     with pytest.raises(isa.IsaError) as e:
         isa.isa_plan_create(**args)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("alpha_ns", [0.0, 0.0625, 0.3, 1.0])
+def test_block_mask_count_and_workspace(alpha_ns):
+    # the count follows the oracle's rounding (R21); the mask adds the coarse
+    # logits and the per-block lists to the workspace only when it is used
+    base = isa.isa_plan_create(1, 3, 4096, 4096, 128, 64, 0.25, 0.5)
+    p = isa.isa_plan_create(1, 3, 4096, 4096, 128, 64, 0.25, 0.5, alpha_ns)
+    n_kv = p.info["n_kv_blocks"]
+    assert n_kv == 64 + 16
+    assert p.info["n_ns"] == orc.ns_count(alpha_ns, n_kv)
+    extra = p.info["workspace_bytes"] - base.info["workspace_bytes"]
+    if p.info["n_ns"] == 0:
+        assert extra == 0
+    else:
+        need = 3 * 128 * 128 * 8 + 3 * p.info["n_flat"] * p.info["n_ns"] * 4
+        assert need <= extra <= need + 512
+
+
+def test_backward_with_block_mask_unsupported():
+    lib = isa._lib()
+    p = isa.isa_plan_create(1, 2, 256, 256, 128, 64, 0.5, 0.5, 0.25)
+    fake = ctypes.c_void_p(0x1000)
+    a = isa.isa_aux_t()
+    a.sel = a.flat = a.sharp = 0x1000
+    st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
+                          fake, fake, fake, fake, 1 << 40, None)
+    assert st == isa.ISA_ERR_UNSUPPORTED
 
 
 def test_null_arguments_rejected_before_any_launch():
