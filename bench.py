@@ -11,7 +11,10 @@ Prints ONE JSON line with the latency, the dense-equivalent TFLOP/s
 (4 B H N^2 D / latency), the per-stage times (HIP events recorded between the
 stages on the launch stream, inside the timed region), the roofline of the
 dominant kernel (the exact path), the library's own dense attention on the same
-input, and the fp64 CPU oracle timed on a bounded sample.
+input, and the fp64 CPU oracle timed on a bounded sample.  Two extra sections
+time the same workload with the block mask inside flat query blocks
+(alpha_ns, default 0.0625) and the decision-frozen backward of the B=2
+N=16384 workload.
 """
 
 import argparse
@@ -54,6 +57,11 @@ def parse():
     ap.add_argument("--bwd-config", type=int, default=5,
                     help="workload of the backward measurement (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--mask-alpha-ns", type=float, default=0.0625,
+                    help="also time the forward with this block-mask ratio (0 = skip)")
+    ap.add_argument("--mask-steps", type=int, default=10)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the workload line: ISA vs dense over N = 5K..64K")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, launch a plain 256 MiB fp32 copy kernel (x2 scale) "
                          "whose FETCH_SIZE / WRITE_SIZE calibrate the HBM counters")
@@ -193,6 +201,106 @@ def bench_backward(args, isa, torch, dev):
             "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12}
 
 
+def bench_block_mask(args, isa, torch, q, k, v, c):
+    """The same workload with the block mask inside flat query blocks
+    (alpha_ns > 0): latency, stage times and the flat-path kernel's rate."""
+    B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
+    N = L_src + L_ctx
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"],
+                               args.mask_alpha_ns)
+    info = plan.info
+    ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for _ in range(3):
+        isa.isa_forward(plan, q, k, v, o, lse, workspace=ws)
+    n_ev = isa.ISA_PROFILE_STAGES + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.mask_steps)]
+    for evs in events:
+        for ev in evs:
+            ev.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.mask_steps):
+        isa.isa_forward(plan, q, k, v, o, lse, workspace=ws, events=events[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.mask_steps
+    stage_ms = {name: float(np.mean([evs[j].elapsed_time(evs[j + 1]) for evs in events]))
+                for j, name in enumerate(isa.STAGE_NAMES)}
+    # flat rows: n_ns * b exact keys plus n_kv - n_ns representative rows each
+    flat_keys = info["n_ns"] * b + info["n_kv_blocks"] - info["n_ns"]
+    flat_flops = 4.0 * B * H * info["n_flat"] * b * flat_keys * D
+    fl_ms = stage_ms["attn_taylor"]
+    _log(f"block mask alpha_ns {args.mask_alpha_ns}: ISA forward {ms:.3f} ms; flat path "
+         f"{fl_ms:.3f} ms")
+    return {"alpha_ns": args.mask_alpha_ns, "n_ns": info["n_ns"], "latency_ms": ms,
+            "dense_equiv_tflops": 4.0 * B * H * N * N * D / (ms * 1e-3) / 1e12,
+            "stages_ms": stage_ms,
+            "flat_path": {"kernel": "attn_flat_bf16_kernel<128>", "ms": fl_ms,
+                          "algorithmic_tflop": flat_flops / 1e12,
+                          "TFLOP/s": flat_flops / (fl_ms * 1e-3) / 1e12,
+                          "mfma_frac": flat_flops / (fl_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+
+
+SWEEP_N = (5120, 8192, 16384, 32768, 51200, 65536)
+
+
+def sweep(args):
+    """ISA forward vs the library's dense attention over the sequence lengths
+    the pages work at (5K-50K tokens, about 64K at 544x960): B=1, H=40, D=128,
+    L_src = L_ctx = N/2, the 32K workload's ratios, seeded ICL-structured inputs
+    (one seed per N).  Prints one JSON line with one entry per N."""
+    import torch
+
+    import sparse_attention_context_block_amd as isa
+    from synth import generate
+
+    dev = torch.device("cuda:0")
+    a_s = 0.25 if args.alpha_s is None else args.alpha_s
+    a_f = 0.5 if args.alpha_f is None else args.alpha_f
+    B, H, D, b = 1, 40, 128, 64
+    rows = []
+    for N in SWEEP_N:
+        inp = generate(B, H, N // 2, N // 2, D, b, seed=2000 + N // 1024, variant="icl")
+        to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = (to_gpu(inp[x]) for x in ("q", "k", "v"))
+        del inp
+        plan = isa.isa_plan_create(B, H, N // 2, N // 2, D, b, a_s, a_f)
+        ws = torch.empty(plan.info["workspace_bytes"], dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def timed(fn, n):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        ims = timed(lambda: isa.isa_forward(plan, q, k, v, o, lse, workspace=ws), args.steps)
+        dms = timed(lambda: isa.isa_dense_forward(q, k, v, o, lse), max(2, args.dense_steps))
+        dense_flops = 4.0 * B * H * N * N * D
+        rows.append({"N": N, "k": plan.info["k"], "l_new": plan.info["l_new"],
+                     "isa_ms": ims, "dense_ms": dms, "speedup": dms / ims,
+                     "isa_dense_equiv_tflops": dense_flops / (ims * 1e-3) / 1e12,
+                     "dense_tflops": dense_flops / (dms * 1e-3) / 1e12})
+        _log(f"N={N}: ISA {ims:.3f} ms, dense {dms:.3f} ms, speedup {dms / ims:.2f}x")
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "ISA forward vs dense attention", "B": B, "H": H, "D": D,
+                      "block": b, "alpha_s": a_s, "alpha_f": a_f, "steps": args.steps,
+                      "dtype": "bf16", "data": "synthetic (seeded [source|context] generator)",
+                      "rows": rows}), flush=True)
+
+
 def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_pp_kernel<128>"):
     """Traffic file text: per-launch HBM bytes of `kernel`, from rocprofv3
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on
@@ -239,6 +347,9 @@ def main():
         print(f"bench.py runs on one GPU only (ISA is independent per head; see the sharding "
               f"note in DESIGN.md); --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
 
@@ -288,6 +399,10 @@ def main():
     stage_ms = {name: float(np.mean([evs[j].elapsed_time(evs[j + 1]) for evs in events]))
                 for j, name in enumerate(isa.STAGE_NAMES)}
     _log(f"ISA forward {ms:.3f} ms/step; stages {stage_ms}")
+
+    block_mask = None
+    if args.mask_alpha_ns > 0:
+        block_mask = bench_block_mask(args, isa, torch, q, k, v, c)
 
     dense = None
     if not args.no_dense:
@@ -350,6 +465,7 @@ def main():
         "dense_baseline": dense,
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
         "roofline": roofline,
+        "block_mask": block_mask,
         "backward": backward,
         "cpu_baseline": cpu,
     }
