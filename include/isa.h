@@ -25,9 +25,12 @@
  *     device-to-host copy happens inside an entry point.
  *   - Argument errors are detected on the host before the first launch, so
  *     on error nothing has been written.  No entry point aborts or throws.
- *   - Supported on the device: block = 64, D in {64, 128}, L_src and L_ctx
- *     multiples of 64, dtype BF16 (fp32 accumulation) or FP32.  Other valid
- *     descriptions return ISA_ERR_UNSUPPORTED.
+ *   - Supported on the device: block = 64, D in {64, 128}, any L_src >= 1 and
+ *     L_ctx >= 0 (the source and the context are each cut into 64-token
+ *     blocks from their own start, so the last block of each may be partial:
+ *     [notes] key design 1 counts ceil(L_ctx / b) context blocks), dtype BF16
+ *     (fp32 accumulation) or FP32.  Other valid descriptions return
+ *     ISA_ERR_UNSUPPORTED.
  */
 #ifndef ISA_H
 #define ISA_H
@@ -73,7 +76,8 @@ typedef struct {
   int64_t n_q_blocks;     /* n_src + n_ctx (query blocks = key blocks) */
   int64_t k;              /* selected context blocks, ceil(alpha_s * n_ctx) */
   int64_t n_kv_blocks;    /* blocks of K_new: n_src + k */
-  int64_t l_new;          /* tokens of K_new: L_src + k * b */
+  int64_t l_new;          /* tokens of K_new: L_src + k * b (fewer when the     */
+                          /* context's partial last block is among the kept)   */
   int64_t n_flat;         /* query blocks on the Taylor path, floor(alpha_f * n_q) */
   int64_t n_sharp;        /* query blocks on the exact path, n_q - n_flat */
   size_t workspace_bytes; /* device workspace isa_forward needs */
@@ -99,8 +103,7 @@ typedef struct {
  * The plan is immutable and may be shared across threads and streams.
  * Errors: ISA_ERR_INVALID_ARG (null out/desc, B/H/D/block < 1 or negative,
  * L_src < 1, L_ctx < 0, a ratio outside [0, 1] or NaN),
- * ISA_ERR_UNSUPPORTED (block != 64, D not 64/128, L_src or L_ctx not a
- * multiple of 64, unknown dtype). */
+ * ISA_ERR_UNSUPPORTED (block != 64, D not 64/128, unknown dtype). */
 isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc);
 
 /* Copy the derived sizes into *info.  Host only. */
@@ -155,7 +158,8 @@ isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K,
  * order given].  sel: device [B, H, k] int32 (as written by isa_forward).
  * isa_forward itself never materialises K_new: its attention kernels read
  * the same rows through the block table.  Errors: ISA_ERR_INVALID_ARG,
- * ISA_ERR_HIP. */
+ * ISA_ERR_UNSUPPORTED (L_src or L_ctx not a multiple of 64: the length of
+ * K_new would depend on sel), ISA_ERR_HIP. */
 isa_status_t isa_gather(isa_plan_t plan, const void* K, const void* V, const int32_t* sel,
                         void* K_new, void* V_new, void* stream);
 
@@ -176,8 +180,9 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * selected receive zero.  Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D]; lse:
  * [B, H, N] float from the forward; aux: sel, flat and sharp from the
  * forward (required).  workspace: at least isa_backward_workspace_bytes().
- * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, or a plan with
- * n_ns > 0), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
+ * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, a plan with
+ * n_ns > 0, or L_src / L_ctx not a multiple of 64), ISA_ERR_WORKSPACE,
+ * ISA_ERR_HIP. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

@@ -23,6 +23,8 @@ struct isa_plan_s {
   WorkspaceLayout ws;
   int64_t N;
   int32_t BH;
+  BlockGrid grid;   // token layout of the blocks
+  bool aligned;     // L_src and L_ctx are multiples of the block length
 };
 
 namespace {
@@ -94,7 +96,6 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   if (d.dtype != ISA_DTYPE_BF16 && d.dtype != ISA_DTYPE_FP32) return ISA_ERR_INVALID_ARG;
   if ((int64_t)d.L_src + d.L_ctx > INT32_MAX / 2) return ISA_ERR_UNSUPPORTED;
   if (d.block != kBlock || (d.D != 64 && d.D != 128)) return ISA_ERR_UNSUPPORTED;
-  if (d.L_src % kBlock != 0 || d.L_ctx % kBlock != 0) return ISA_ERR_UNSUPPORTED;
   const int64_t BH = (int64_t)d.B * d.H;
   if (BH > 65535) return ISA_ERR_UNSUPPORTED;
 
@@ -104,6 +105,7 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   p->d = d;
   p->BH = (int32_t)BH;
   p->N = (int64_t)d.L_src + d.L_ctx;
+  p->aligned = d.L_src % kBlock == 0 && d.L_ctx % kBlock == 0;
   isa_plan_info_t& in = p->info;
   in.n_src_blocks = (d.L_src + d.block - 1) / d.block;
   in.n_ctx_blocks = (d.L_ctx + d.block - 1) / d.block;
@@ -118,6 +120,9 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   in.n_flat = flat_count(d.alpha_f, in.n_q_blocks);
   in.n_sharp = in.n_q_blocks - in.n_flat;
   in.n_ns = ns_count(d.alpha_ns, in.n_kv_blocks);
+  p->grid.L_src = d.L_src;
+  p->grid.n_src = (int32_t)in.n_src_blocks;
+  p->grid.N = (int32_t)p->N;
 
   WorkspaceLayout& w = p->ws;
   size_t off = 0;
@@ -242,7 +247,7 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   pe.n_q_entries = (int)in.n_sharp;
   pe.kv_tab = kv_tab;
   pe.kv_tab_stride = in.n_kv_blocks;
-  pe.kv_rows = (int)in.l_new;
+  pe.kv_rows = (int)in.n_kv_blocks * kBlock;  // one 64-row tile per K_new block
   pe.kv_row_shift = 6;
   pe.q_head_stride = plan->N * D;
   pe.kv_head_stride = plan->N * D;
@@ -251,6 +256,7 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   pe.D = D;
   pe.scale_log2 = scale_log2;
   pe.lse_offset = 0.0f;
+  pe.grid = plan->grid;
   ISA_LAUNCH(launch_attention(pe, d.dtype, s));
   ISA_STAGE(5);
 
@@ -282,6 +288,7 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
     pf.scale_log2 = scale_log2;
     pf.exact_bias_log2 = (float)(-log2((double)d.block));
     pf.lse_offset = (float)log((double)d.block);
+    pf.grid = plan->grid;
     ISA_LAUNCH(launch_attention_flat(pf, d.dtype, s));
     ISA_STAGE(6);
     return ISA_OK;
@@ -326,6 +333,7 @@ isa_status_t isa_gather(isa_plan_t plan, const void* K, const void* V, const int
   if (!K || !V || !K_new || !V_new || (!sel && plan->info.k > 0)) return ISA_ERR_INVALID_ARG;
   if (!aligned16(K) || !aligned16(V) || !aligned16(K_new) || !aligned16(V_new))
     return ISA_ERR_INVALID_ARG;
+  if (!plan->aligned) return ISA_ERR_UNSUPPORTED;  // K_new's length would depend on sel
   const isa_plan_desc_t& d = plan->d;
   ISA_LAUNCH(launch_gather(K, V, sel, d.dtype, plan->BH, (int)plan->N, d.D,
                            (int)plan->info.n_src_blocks, (int)plan->info.k, d.block, K_new, V_new,
@@ -359,6 +367,9 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
   p.BH = B * H;
   p.D = D;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  p.grid.L_src = N;  // no context: a plain grid of whole blocks
+  p.grid.n_src = N / kBlock;
+  p.grid.N = N;
   ISA_LAUNCH(launch_attention(p, dtype, static_cast<hipStream_t>(stream)));
   return ISA_OK;
 }
@@ -415,6 +426,7 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
     if (!aligned16(q)) return ISA_ERR_INVALID_ARG;
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
   if (plan->info.n_ns > 0 && plan->info.n_flat > 0) return ISA_ERR_UNSUPPORTED;
+  if (!plan->aligned) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);

@@ -82,7 +82,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const int e = qt * 2 + (wave >> 1);
   const bool wave_valid = e < p.n_q_entries;
   const int qblk = wave_valid ? (p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e) : 0;
-  const int64_t qrow = (int64_t)qblk * kBlock + (wave & 1) * 32 + l32;
+  // row qr of the query block; the tail rows of a partial block (last block of
+  // a segment) read its first row and are not stored
+  const int qr = (wave & 1) * 32 + l32;
+  const bool q_ok = qr < p.grid.rows(qblk);
+  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
@@ -100,17 +104,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   // block-table entry of the tile to load next, prefetched one tile ahead so
   // its scalar load latency hides behind a whole tile of compute
   int next_blk = (tab && !row_table) ? tab[0] : 0;
+  int tile_last = kBN - 1;  // last valid row of the block being loaded
   auto tile_row0 = [&](int t) -> int64_t {
-    if (!tab) return (int64_t)t * kBN;
+    const int blk = tab ? next_blk : t;
     if (row_table) return 0;
-    const int64_t r0 = (int64_t)next_blk * kBN;
-    next_blk = (t + 1 < n_tiles) ? tab[t + 1] : 0;
+    tile_last = p.grid.rows(blk) - 1;
+    const int64_t r0 = p.grid.start(blk);
+    if (tab) next_blk = (t + 1 < n_tiles) ? tab[t + 1] : 0;
     return r0;
   };
   auto src_row = [&](int64_t row0, int t, int r) -> int64_t {
-    if (!row_table) return row0 + r;  // contiguous (block tiles are always full)
+    if (!row_table) return row0 + min(r, tile_last);  // a partial block repeats its last row
     return tab[min(t * kBN + r, p.kv_rows - 1)];  // rows past the end: valid, then masked
   };
+  // Partial blocks (the tail of each segment).  Block-table tiles: the source
+  // tail sits at K_new position n_src - 1, the context tail (if kept) last;
+  // their missing keys are masked.  Row table (pooled rows): the same two
+  // positions carry the weight (tokens / kBlock) as a logit offset.
+  const int src_tail = p.grid.src_tail();
+  const int ctx_tail = p.grid.ctx_tail();
+  const int n_pos = row_table ? p.kv_rows : n_tiles;
+  const int pt0 = (tab && src_tail) ? p.grid.n_src - 1 : -1;
+  const int pt1 = (tab && ctx_tail && tab[n_pos - 1] == p.grid.n_blocks() - 1) ? n_pos - 1 : -1;
+  const float w0 = src_tail ? log2f((float)src_tail / kBN) / p.scale_log2 : 0.0f;
+  const float w1 = ctx_tail ? log2f((float)ctx_tail / kBN) / p.scale_log2 : 0.0f;
 
   // staging registers for the next tile (named, so they stay in VGPRs)
   uint4 k0, k1, k2, k3;  // K chunks c = tid + 256 i (i < KCH <= 4)
@@ -226,6 +243,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
           if (key >= valid) sacc[s][r] = -INFINITY;
         }
     }
+    if (kRowTable) {
+      // weight of a partial block's pooled row
+      const int u0 = pt0 - t * kBN, u1 = pt1 - t * kBN;
+      if ((pt0 >= 0 && u0 >= 0 && u0 < kBN) || (pt1 >= 0 && u1 >= 0 && u1 < kBN)) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key == u0) sacc[s][r] += w0;
+            if (key == u1) sacc[s][r] += w1;
+          }
+      }
+    } else {
+      const int vt = (t == pt0) ? src_tail : ((t == pt1) ? ctx_tail : kBN);
+      if (vt < kBN) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= vt) sacc[s][r] = -INFINITY;
+          }
+      }
+    }
 
     // online softmax (exp2 domain); lane and lane^32 hold the same query
     float tmax = sacc[0][0];
@@ -294,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const float inv = 1.0f / l_run;
   bf16_bits* Oh = static_cast<bf16_bits*>(p.o) + bh * p.q_head_stride + qrow * D;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) {
+  for (int j = 0; j < ND && q_ok; ++j) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x2_t a, b;
@@ -308,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
       *reinterpret_cast<uint2*>(Oh + 32 * j + 8 * g + 4 * hi) = w;
     }
   }
-  if (p.lse && hi == 0) {
+  if (p.lse && hi == 0 && q_ok) {
     p.lse[bh * p.lse_head_stride + qrow] =
         (m_run + __log2f(l_run)) * 0.69314718055994531f + p.lse_offset;
   }

@@ -25,13 +25,24 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int row = tid >> 2, part = tid & 3;
   const int qblk = p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e;
-  const int64_t qrow = (int64_t)qblk * kBlock + row;
+  // the tail rows of a partial query block read its first row and are not stored
+  const bool q_ok = row < p.grid.rows(qblk);
+  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? row : 0);
   const float* Qh = static_cast<const float*>(p.q) + bh * p.q_head_stride;
   const float* Kh = static_cast<const float*>(p.k) + bh * p.kv_head_stride;
   const float* Vh = static_cast<const float*>(p.v) + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
   const int shift = p.kv_row_shift;
   const int rmask = (1 << shift) - 1;
+  // Partial blocks (the tail of each segment) sit at K_new positions n_src - 1
+  // and, if the context tail is kept, last.  Block table: their missing tokens
+  // are skipped; row table (pooled rows): they carry the weight (tokens / b).
+  const int src_tail = p.grid.src_tail(), ctx_tail = p.grid.ctx_tail();
+  const int n_pos = shift ? (p.kv_rows >> shift) : p.kv_rows;
+  const int pu0 = (tab && src_tail) ? p.grid.n_src - 1 : -1;
+  const int pu1 = (tab && ctx_tail && tab[n_pos - 1] == p.grid.n_blocks() - 1) ? n_pos - 1 : -1;
+  const float lw0 = src_tail ? logf((float)src_tail / kBlock) : 0.0f;
+  const float lw1 = ctx_tail ? logf((float)ctx_tail / kBlock) : 0.0f;
 
   float q[DP], o[DP];
 #pragma unroll
@@ -48,18 +59,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
     for (int i = tid; i < kTile * (D / 4); i += kThreads) {
       const int r = i / (D / 4), c = (i % (D / 4)) * 4;
       int rr = min(t0 + r, p.kv_rows - 1);
-      const int64_t src = tab ? ((int64_t)tab[rr >> shift] << shift) + (rr & rmask) : rr;
+      int64_t src = rr;
+      if (tab && shift) {
+        const int blk = tab[rr >> shift];
+        src = (int64_t)p.grid.start(blk) + min(rr & rmask, p.grid.rows(blk) - 1);
+      } else if (tab) {
+        src = tab[rr];
+      }
       *reinterpret_cast<float4*>(&Ks[r][c]) = *reinterpret_cast<const float4*>(Kh + src * D + c);
       *reinterpret_cast<float4*>(&Vs[r][c]) = *reinterpret_cast<const float4*>(Vh + src * D + c);
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
+      const int rr = t0 + j;
+      float wbias = 0.0f;
+      if (tab && shift) {
+        const int pos = rr >> shift;
+        const int vt = (pos == pu0) ? src_tail : ((pos == pu1) ? ctx_tail : kBlock);
+        if ((rr & rmask) >= vt) continue;  // past a partial block's tail
+      } else if (tab) {
+        wbias = (rr == pu0) ? lw0 : ((rr == pu1) ? lw1 : 0.0f);
+      }
       float s = 0.0f;
 #pragma unroll
       for (int i = 0; i < DP; ++i) s = fmaf(q[i], Ks[j][part * DP + i], s);
       s += __shfl_xor(s, 1);
       s += __shfl_xor(s, 2);
-      s *= scale;
+      s = s * scale + wbias;
       const float m_new = fmaxf(m, s);
       const float alpha = expf(m - m_new);
       const float pj = expf(s - m_new);
@@ -69,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
       m = m_new;
     }
   }
+  if (!q_ok) return;
   const float inv = 1.0f / l;
   float* Oh = static_cast<float*>(p.o) + bh * p.q_head_stride;
 #pragma unroll

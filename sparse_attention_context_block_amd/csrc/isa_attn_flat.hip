@@ -73,7 +73,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
 
   // ---- this wave's 32 query rows ----
   const int qblk = p.flat[bh * p.n_flat + f];
-  const int64_t qrow = (int64_t)qblk * kBlock + wave * 32 + l32;
+  // the tail rows of a partial query block read its first row and are not stored
+  const int qr = wave * 32 + l32;
+  const bool q_ok = qr < p.grid.rows(qblk);
+  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
@@ -90,9 +93,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
   // source row r of tile t (exact tiles: rows of K/V; representative tiles:
   // rows of K^c/V^c, past-the-end rows clamped to a valid row and masked later)
   auto src_row = [&](int t, int r) -> int64_t {
-    if (t < n_ns) return (int64_t)tab[ns[t]] * kBN + r;
+    if (t < n_ns) {
+      const int blk = tab[ns[t]];  // a partial block repeats its last row
+      return (int64_t)p.grid.start(blk) + min(r, p.grid.rows(blk) - 1);
+    }
     return tab[min((t - n_ns) * kBN + r, n_kv - 1)];
   };
+  // Partial blocks (the tail of each segment) sit at K_new positions n_src - 1
+  // and, if the context tail is kept, n_kv - 1: taken exactly, their missing
+  // tokens are masked; as representatives they carry the weight (tokens / b).
+  const int src_tail = p.grid.src_tail();
+  const int ctx_tail = p.grid.ctx_tail();
+  const int pu0 = src_tail ? p.grid.n_src - 1 : -1;
+  const int pu1 = (ctx_tail && tab[n_kv - 1] == p.grid.n_blocks() - 1) ? n_kv - 1 : -1;
+  const float w0 = src_tail ? log2f((float)src_tail / kBN) / p.scale_log2 : 0.0f;
+  const float w1 = ctx_tail ? log2f((float)ctx_tail / kBN) / p.scale_log2 : 0.0f;
 
   u32x4 kst[KCH];
   u32x4 vst[4 * VCH];
@@ -175,7 +190,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
         sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[s], 0, 0, 0);
       }
     }
-    // representative tiles: mask rows past n_kv and blocks taken exactly
+    // representative tiles: mask rows past n_kv and blocks taken exactly, and
+    // weight a partial block's row; exact tiles: mask a partial block's tail
     if (!exact) {
       const int u0 = (t - n_ns) * kBN;
 #pragma unroll
@@ -183,8 +199,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int u = u0 + 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (u == pu0) sacc[s][r] += w0;
+          if (u == pu1) sacc[s][r] += w1;
           if (u >= n_kv || ((mask[u >> 5] >> (u & 31)) & 1u)) sacc[s][r] = -INFINITY;
         }
+    } else {
+      const int pos = ns[t];
+      const int vt = (pos == pu0) ? src_tail : ((pos == pu1) ? ctx_tail : kBN);
+      if (vt < kBN) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= vt) sacc[s][r] = -INFINITY;
+          }
+      }
     }
     const float bias2 = exact ? exact_bias2 : 0.0f;
 
@@ -247,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
   const float inv = 1.0f / l_run;
   bf16_bits* Oh = static_cast<bf16_bits*>(p.o) + bh * p.q_head_stride + qrow * D;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) {
+  for (int j = 0; j < ND && q_ok; ++j) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x2_t a, b;
@@ -261,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
       *reinterpret_cast<uint2*>(Oh + 32 * j + 8 * g + 4 * hi) = w;
     }
   }
-  if (p.lse && hi == 0) {
+  if (p.lse && hi == 0 && q_ok) {
     p.lse[bh * p.lse_head_stride + qrow] =
         (m_run + __log2f(l_run)) * 0.69314718055994531f + p.lse_offset;
   }
@@ -290,7 +320,8 @@ __global__ __launch_bounds__(kF32Threads) void attn_flat_f32_kernel(FlatParams p
   for (int t = tid; t < n_ns; t += kF32Threads) atomicOr(&mask[ns[t] >> 5], 1u << (ns[t] & 31));
 
   const int qblk = p.flat[bh * p.n_flat + f];
-  const int64_t qrow = (int64_t)qblk * kBlock + row;
+  const bool q_ok = row < p.grid.rows(qblk);
+  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? row : 0);
   const float* Qh = static_cast<const float*>(p.q) + bh * p.q_head_stride;
   const float* Kh = static_cast<const float*>(p.k) + bh * p.kv_head_stride;
   const float* Vh = static_cast<const float*>(p.v) + bh * p.kv_head_stride;
@@ -304,6 +335,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_flat_f32_kernel(FlatParams p
   }
   const float scale = p.scale_log2 * 0.69314718055994531f;     // 1 / sqrt(D)
   const float bias = p.exact_bias_log2 * 0.69314718055994531f;  // -ln(b)
+  const int src_tail = p.grid.src_tail(), ctx_tail = p.grid.ctx_tail();
+  const int pu0 = src_tail ? p.grid.n_src - 1 : -1;
+  const int pu1 = (ctx_tail && tab[n_kv - 1] == p.grid.n_blocks() - 1) ? n_kv - 1 : -1;
+  const float lw0 = src_tail ? logf((float)src_tail / kBlock) : 0.0f;
+  const float lw1 = ctx_tail ? logf((float)ctx_tail / kBlock) : 0.0f;
   const int n_exact_rows = n_ns * kBlock;
   const int n_rows = n_exact_rows + n_kv;
   float m = -INFINITY, l = 0.0f;
@@ -314,8 +350,13 @@ __global__ __launch_bounds__(kF32Threads) void attn_flat_f32_kernel(FlatParams p
       const int r = i / (D / 4), c = (i % (D / 4)) * 4;
       const int rr = min(t0 + r, n_rows - 1);
       const bool ex = rr < n_exact_rows;
-      const int64_t src = ex ? (int64_t)tab[ns[rr / kBlock]] * kBlock + rr % kBlock
-                             : (int64_t)tab[rr - n_exact_rows];
+      int64_t src;
+      if (ex) {
+        const int blk = tab[ns[rr / kBlock]];
+        src = (int64_t)p.grid.start(blk) + min(rr % kBlock, p.grid.rows(blk) - 1);
+      } else {
+        src = tab[rr - n_exact_rows];
+      }
       const float* kb = ex ? Kh : Kch;
       const float* vb = ex ? Vh : Vch;
       *reinterpret_cast<float4*>(&Ks[r][c]) = *reinterpret_cast<const float4*>(kb + src * D + c);
@@ -325,16 +366,22 @@ __global__ __launch_bounds__(kF32Threads) void attn_flat_f32_kernel(FlatParams p
     for (int j = 0; j < n; ++j) {
       const int rr = t0 + j;
       const bool ex = rr < n_exact_rows;
+      float wbias = 0.0f;
       if (!ex) {
         const int u = rr - n_exact_rows;
         if ((mask[u >> 5] >> (u & 31)) & 1u) continue;  // taken exactly
+        wbias = (u == pu0) ? lw0 : ((u == pu1) ? lw1 : 0.0f);
+      } else {
+        const int pos = ns[rr / kBlock];
+        const int vt = (pos == pu0) ? src_tail : ((pos == pu1) ? ctx_tail : kBlock);
+        if (rr % kBlock >= vt) continue;  // past a partial block's tail
       }
       float s = 0.0f;
 #pragma unroll
       for (int i = 0; i < DP; ++i) s = fmaf(q[i], Ks[j][part * DP + i], s);
       s += __shfl_xor(s, 1);
       s += __shfl_xor(s, 2);
-      s = s * scale + (ex ? bias : 0.0f);
+      s = s * scale + (ex ? bias : wbias);
       const float m_new = fmaxf(m, s);
       const float alpha = expf(m - m_new);
       const float pj = expf(s - m_new);
@@ -344,6 +391,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_flat_f32_kernel(FlatParams p
       m = m_new;
     }
   }
+  if (!q_ok) return;
   const float inv = 1.0f / l;
   float* Oh = static_cast<float*>(p.o) + bh * p.q_head_stride;
 #pragma unroll

@@ -83,7 +83,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   const int e = qt * 4 + (wave >> 1);
   const bool wave_valid = e < p.n_q_entries;
   const int qblk = wave_valid ? (p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e) : 0;
-  const int64_t qrow = (int64_t)qblk * kBlock + (wave & 1) * 32 + l32;
+  // row qr of the query block; the tail rows of a partial block (last block of
+  // a segment) read its first row and are not stored
+  const int qr = (wave & 1) * 32 + l32;
+  const bool q_ok = qr < p.grid.rows(qblk);
+  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
@@ -94,8 +98,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   const bf16_bits* Kh = static_cast<const bf16_bits*>(p.k) + bh * p.kv_head_stride;
   const bf16_bits* Vh = static_cast<const bf16_bits*>(p.v) + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
-  const int n_tiles = p.kv_rows / kBN;  // exact path and dense: always whole tiles
+  const int n_tiles = p.kv_rows / kBN;  // exact path and dense: one tile per block
   auto blk_of = [&](int u) -> int { return tab ? tab[u] : u; };
+  // tiles holding a partial block: the source tail sits at K_new position
+  // n_src - 1, the context tail (if kept) last; their missing keys are masked
+  const int src_tail = p.grid.src_tail();
+  const int ctx_tail = p.grid.ctx_tail();
+  const int pt0 = src_tail ? p.grid.n_src - 1 : -1;
+  const int pt1 =
+      (ctx_tail && tab && tab[n_tiles - 1] == p.grid.n_blocks() - 1) ? n_tiles - 1 : -1;
 
   // group A stages K: chunk c = gtid + 256 i -> row c / KC, column chunk c % KC
   uint4 k0, k1, k2, k3;
@@ -110,11 +121,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   auto v_lds = [&](int b) { return smem + 2 * S::kKBytes + b * S::kVBytes; };
 
   auto load_k = [&](int blk) __attribute__((always_inline)) {
-    const bf16_bits* base = Kh + (int64_t)blk * kBN * D;
+    const bf16_bits* base = Kh + (int64_t)p.grid.start(blk) * D;
+    const int last = p.grid.rows(blk) - 1;  // rows past a partial block repeat its last row
 #define ISA_K_LOAD(I, R)                                                                \
   {                                                                                     \
     const int c = gtid + kGroup * I;                                                    \
-    R = *reinterpret_cast<const uint4*>(base + (c / KC) * D + (c % KC) * 8);            \
+    R = *reinterpret_cast<const uint4*>(base + min(c / KC, last) * D + (c % KC) * 8);            \
   }
     ISA_K_LOAD(0, k0)
     ISA_K_LOAD(1, k1)
@@ -141,11 +153,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   };
   auto load_v = [&](int blk) __attribute__((always_inline)) {
     if (v_active) {
-      const bf16_bits* vb = Vh + ((int64_t)blk * kBN + 4 * vg) * D + vd * 8;
-      v0 = *reinterpret_cast<const uint4*>(vb);
-      v1 = *reinterpret_cast<const uint4*>(vb + D);
-      v2 = *reinterpret_cast<const uint4*>(vb + 2 * D);
-      v3 = *reinterpret_cast<const uint4*>(vb + 3 * D);
+      const bf16_bits* vb = Vh + (int64_t)p.grid.start(blk) * D + vd * 8;
+      const int last = p.grid.rows(blk) - 1;
+      v0 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 0, last) * D);
+      v1 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 1, last) * D);
+      v2 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 2, last) * D);
+      v3 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 3, last) * D);
     }
   };
   auto store_v = [&](int b) __attribute__((always_inline)) {
@@ -192,7 +205,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
     }
   };
   // online softmax of sacc (exp2 domain) into the packed P^T operands
-  auto softmax = [&]() __attribute__((always_inline)) {
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int vt = (t == pt0) ? src_tail : ((t == pt1) ? ctx_tail : kBN);
+    if (vt < kBN) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= vt) sacc[s][r] = -INFINITY;
+        }
+    }
     float tmax = sacc[0][0];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -270,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
 
   // ---- main loop: VALU phase, barrier, MFMA phase, barrier ----
   for (int t = 0; t < n_tiles; ++t) {
-    softmax();
+    softmax(t);
     if (t + 1 < n_tiles) {
       const int ent = e_next;
       e_next = blk_of(min(t + 3, n_tiles - 1));
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   const float inv = 1.0f / l_run;
   bf16_bits* Oh = static_cast<bf16_bits*>(p.o) + bh * p.q_head_stride + qrow * D;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) {
+  for (int j = 0; j < ND && q_ok; ++j) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x2_t a, b;
@@ -317,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
       *reinterpret_cast<uint2*>(Oh + 32 * j + 8 * g + 4 * hi) = w;
     }
   }
-  if (p.lse && hi == 0) {
+  if (p.lse && hi == 0 && q_ok) {
     p.lse[bh * p.lse_head_stride + qrow] =
         (m_run + __log2f(l_run)) * 0.69314718055994531f + p.lse_offset;
   }

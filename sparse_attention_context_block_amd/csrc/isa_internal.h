@@ -18,6 +18,32 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 // also the key-tile height of the attention kernels).
 constexpr int kBlock = 64;
 
+// Block grid of a [source | context] sequence ([notes] key design 1 counts
+// ceil(L_ctx / b) context blocks): the source and the context are each cut
+// into kBlock-token blocks from their own start, so the last block of each
+// segment may be partial.  Block b starts at kBlock * b (b < n_src) or at
+// L_src + kBlock * (b - n_src) and holds min(kBlock, segment end - start)
+// tokens.  A sequence without context (L_src = N) is a plain grid.
+struct BlockGrid {
+  int32_t L_src;  // tokens of the source segment
+  int32_t n_src;  // its blocks, ceil(L_src / kBlock)
+  int32_t N;      // all tokens
+  __host__ __device__ __forceinline__ int start(int b) const {
+    return b < n_src ? b * kBlock : L_src + (b - n_src) * kBlock;
+  }
+  __host__ __device__ __forceinline__ int rows(int b) const {
+    const int end = b < n_src ? L_src : N;
+    const int n = end - start(b);
+    return n < kBlock ? n : kBlock;
+  }
+  __host__ __device__ __forceinline__ int n_blocks() const {
+    return n_src + (N - L_src + kBlock - 1) / kBlock;
+  }
+  // tokens of the partial last block of each segment (0: the segment is whole)
+  __host__ __device__ __forceinline__ int src_tail() const { return L_src % kBlock; }
+  __host__ __device__ __forceinline__ int ctx_tail() const { return (N - L_src) % kBlock; }
+};
+
 // ---------------------------------------------------------------------------
 // Attention launch description shared by the exact path, the 0-th order
 // Taylor path and the dense baseline.  Queries come in 64-row blocks listed in
@@ -46,6 +72,12 @@ struct AttnParams {
   int32_t D;
   float scale_log2;          // log2(e) / sqrt(D)
   float lse_offset;          // added to every lse (ln of a uniform block weight)
+  // token layout of the query rows (and of the key rows for a block table):
+  // query block e holds grid.rows(e) rows from grid.start(e); a block-table
+  // key tile holds grid.rows(blk) keys, the rest of the tile is masked.  With
+  // a row table the keys are pooled block rows: a partial block's row enters
+  // with the extra weight log of (its tokens / kBlock).
+  BlockGrid grid;
 };
 
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream);
@@ -78,6 +110,7 @@ struct FlatParams {
   float scale_log2;         // log2(e) / sqrt(D)
   float exact_bias_log2;    // -log2(b): exact tokens weigh 1 against b per block
   float lse_offset;         // ln(b)
+  BlockGrid grid;           // token layout of the blocks (partial segment tails)
 };
 hipError_t launch_attention_flat(const FlatParams& p, isa_dtype_t dtype, hipStream_t stream);
 hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int32_t* kv_tab,

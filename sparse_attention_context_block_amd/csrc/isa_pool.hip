@@ -95,13 +95,12 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
   __syncthreads();
 
   const int64_t out = (bh * n_q + blk) * (int64_t)D;
-  const double inv_rows = 1.0 / (double)rows;
   for (int idx = tid; idx < 3 * D; idx += kThreads) {
     const int t = idx / D, d = idx % D;
     double s = 0.0;
 #pragma unroll
     for (int g = 0; g < RP; ++g) s += red[t][g][d];  // fixed order
-    const double mean = (rows == kBlock) ? s * (1.0 / kBlock) : s * inv_rows;
+    const double mean = s / (double)rows;
     if (t == 0) {
       qc[out + d] = mean;
     } else if (t == 1) {

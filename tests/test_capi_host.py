@@ -84,8 +84,6 @@ def test_plan_counts_follow_the_rounding_rule(alpha_s, alpha_f):
     (dict(alpha_s=float("nan")), isa.ISA_ERR_INVALID_ARG),
     (dict(block=32), isa.ISA_ERR_UNSUPPORTED),
     (dict(D=96), isa.ISA_ERR_UNSUPPORTED),
-    (dict(L_src=100), isa.ISA_ERR_UNSUPPORTED),
-    (dict(L_ctx=70), isa.ISA_ERR_UNSUPPORTED),
     (dict(alpha_ns=1.5), isa.ISA_ERR_INVALID_ARG),
     (dict(L_src=64 * 4097, L_ctx=0), isa.ISA_ERR_UNSUPPORTED),
 ])
@@ -112,6 +110,29 @@ def test_block_mask_count_and_workspace(alpha_ns):
     else:
         need = 3 * 128 * 128 * 8 + 3 * p.info["n_flat"] * p.info["n_ns"] * 4
         assert need <= extra <= need + 512
+
+
+@pytest.mark.parametrize("L_src,L_ctx", [(100, 200), (50, 0), (64, 1), (1000, 1000), (4097, 63)])
+def test_partial_blocks_grid(L_src, L_ctx):
+    # each segment is cut from its own start; the counts follow the oracle's grid
+    p = isa.isa_plan_create(1, 2, L_src, L_ctx, 128, 64, 0.5, 0.5)
+    starts, ends, n_src, n_ctx = orc.block_grid(L_src, L_ctx, 64)
+    assert (p.info["n_src_blocks"], p.info["n_ctx_blocks"]) == (n_src, n_ctx)
+    assert p.info["n_q_blocks"] == len(starts)
+    assert p.info["k"] == orc.select_count(0.5, n_ctx)
+    assert p.info["n_flat"] == orc.flat_count(0.5, len(starts))
+
+
+def test_unaligned_gather_and_backward_unsupported():
+    lib = isa._lib()
+    p = isa.isa_plan_create(1, 2, 100, 200, 128, 64, 0.5, 0.5)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.isa_gather(p.handle, fake, fake, fake, fake, fake, None) == isa.ISA_ERR_UNSUPPORTED
+    a = isa.isa_aux_t()
+    a.sel = a.flat = a.sharp = 0x1000
+    st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
+                          fake, fake, fake, fake, 1 << 40, None)
+    assert st == isa.ISA_ERR_UNSUPPORTED
 
 
 def test_backward_with_block_mask_unsupported():
