@@ -89,28 +89,63 @@ struct TR {
   static constexpr int kBytes = D * kStride;
 };
 
+// 16-byte chunk swizzle of the transposed tile: chunk c of row r sits at
+// chunk c ^ tr_swz(r).  With the 16-byte row pad it keeps both the staging
+// stores (one row per 8 dims, 16 threads a row group) and the MFMA operand
+// reads (32 consecutive rows, one chunk) spread over all LDS banks.
+__device__ __forceinline__ int tr_swz(int row) {
+  const int x = (row >> 4) & 7;
+  return x ^ ((x & 1) << 2);
+}
+
+// Byte offsets of the operand reads from a transposed tile: lane (l32, hi)
+// reads chunk 2 C + hi of row 32 j + l32.  With b = bit 4 of the row, the
+// swizzled chunk is (hi ^ b) + 2 ((C ^ j) & 1) + 4 (((C ^ j) >> 1) ^ b), so two
+// per-lane bases and compile-time offsets cover every (j, C).
+template <int D>
+struct TrReader {
+  int base0, base1;
+  __device__ __forceinline__ void init(int l32, int hi) {
+    const int b = (l32 >> 4) & 1;
+    const int common = l32 * TR<D>::kStride + 16 * (hi ^ b);
+    base0 = common + 64 * b;
+    base1 = common + 64 * (1 - b);
+  }
+  __device__ __forceinline__ int off(int j, int C) const {
+    const int k = C ^ j;
+    return ((k >> 1) ? base1 : base0) + 32 * j * TR<D>::kStride + 32 * (k & 1);
+  }
+};
+
 // Staging of one 64-row tile (rows given by row_of(r)) into registers and then
-// into LDS in the row-major and/or the transposed layout.
+// into LDS: row-major only, or row-major and transposed from the same loads.
 template <int D>
 struct TileStager {
   static constexpr int KC = D / 8;                     // 16-byte chunks per row
   static constexpr int KCH = kBN * KC / kThreads;      // row-major chunks per thread
-  u32x4 r0, r1, r2, r3;  // row-major staging: chunk c = tid + 256 i
-  u32x4 t0, t1, t2, t3;  // transposed staging: rows 4 tg + i at chunk td
-  int tg, td;
+  u32x4 r0, r1, r2, r3;  // row-major only: chunk c = tid + 256 i
+  u32x4 t0, t1, t2, t3;  // both layouts: rows 4 tg + i at chunk td
   bool t_active;
-  int tpos;
+  int rm_off, tr_off;    // this thread's store offsets in the two layouts
+  int tg, td;
 
   __device__ __forceinline__ void init(int tid) {
-    tg = tid % (kBN / 4);
-    td = tid / (kBN / 4);
-    t_active = td < KC;
-    const int q = tg & 3;
-    tpos = (tg >> 2) * 16 + (((q & 1) << 1) | (q >> 1)) * 4;
+    // KC consecutive threads read one row (coalesced); the row groups of four
+    // consecutive thread rows go in the order (0, 2, 1, 3), so each 32-lane
+    // half of a transposed store fills whole 16-byte chunks
+    td = tid % KC;
+    const int q = tid / KC;
+    tg = (q & ~3) | (((q & 1) << 1) | ((q >> 1) & 1));
+    t_active = q < kBN / 4;
+    // position of row 4 tg in the transposed layout (quad order (0, 2, 1, 3))
+    const int tq = tg & 3;
+    const int tpos = (tg >> 2) * 16 + (((tq & 1) << 1) | (tq >> 1)) * 4;
+    rm_off = 4 * tg * RM<D>::kStride + td * 16;
+    tr_off = td * 8 * TR<D>::kStride + 16 * ((tpos >> 3) ^ tr_swz(td * 8)) + (tpos & 7) * 2;
   }
-  template <bool kRM, bool kTR, typename RowOf>
+  template <bool kTR, typename RowOf>
   __device__ __forceinline__ void load(const bf16_bits* base, int tid, RowOf row_of) {
-    if constexpr (kRM) {
+    if constexpr (!kTR) {
 #define ISA_LD(I, R)                                                                    \
   {                                                                                     \
     const int c = tid + kThreads * I;                                                   \
@@ -123,8 +158,7 @@ struct TileStager {
         ISA_LD(3, r3)
       }
 #undef ISA_LD
-    }
-    if constexpr (kTR) {
+    } else {
       if (t_active) {
         const bf16_bits* b = base + td * 8;
         t0 = *reinterpret_cast<const u32x4*>(b + row_of(4 * tg + 0) * D);
@@ -134,9 +168,9 @@ struct TileStager {
       }
     }
   }
-  template <bool kRM, bool kTR>
+  template <bool kTR>
   __device__ __forceinline__ void store(unsigned char* rm, unsigned char* tr, int tid) {
-    if constexpr (kRM) {
+    if constexpr (!kTR) {
 #define ISA_ST(I, R)                                                                   \
   {                                                                                    \
     const int c = tid + kThreads * I;                                                  \
@@ -149,10 +183,15 @@ struct TileStager {
         ISA_ST(3, r3)
       }
 #undef ISA_ST
-    }
-    if constexpr (kTR) {
+    } else {
       if (t_active) {
-        unsigned char* row = tr + (td * 8) * TR<D>::kStride + tpos * 2;
+        unsigned char* r = rm + rm_off;
+        *reinterpret_cast<u32x4*>(r) = t0;
+        *reinterpret_cast<u32x4*>(r + RM<D>::kStride) = t1;
+        *reinterpret_cast<u32x4*>(r + 2 * RM<D>::kStride) = t2;
+        *reinterpret_cast<u32x4*>(r + 3 * RM<D>::kStride) = t3;
+        // dims 8 td .. 8 td + 7 share one swizzle (rows 16 apart differ)
+        unsigned char* row = tr + tr_off;
 #define ISA_TS(W, F)                                                                    \
   *reinterpret_cast<uint2*>(row + (2 * W) * TR<D>::kStride) =                          \
       make_uint2(pack2(t0.F, t1.F, false), pack2(t2.F, t3.F, false));                  \
@@ -214,6 +253,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p) {
     qreg[kk] = *reinterpret_cast<const bf16x8_t*>(Qh + qrow * D + 16 * kk + 8 * hi);
     oreg[kk] = *reinterpret_cast<const bf16x8_t*>(dOh + qrow * D + 16 * kk + 8 * hi);
   }
+  // An empty register dependency retires these loads here (one vmcnt wait).
+  // Otherwise the wait pass cannot prove them done inside the loop and waits
+  // for the next tile's prefetch loads before every MFMA that reads them.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm("" : "+v"(qreg[kk]), "+v"(oreg[kk]));
   const float lse2 = (p.lse[bh * p.lse_head_stride + qrow] - p.lse_offset) * 1.4426950408889634f;
   const float dlt = p.delta[bh * p.lse_head_stride + qrow];
 
@@ -225,22 +269,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p) {
   TileStager<D> ks, vs;
   ks.init(tid);
   vs.init(tid);
+  TrReader<D> trr;
+  trr.init(l32, hi);
   auto load = [&](int t) __attribute__((always_inline)) {
     if constexpr (kRowTable) {
       auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return tab[min(t * kBN + r, p.kv_rows - 1)]; };
-      ks.template load<true, true>(Kh, tid, row_of);
-      vs.template load<true, false>(Vh, tid, row_of);
+      ks.template load<true>(Kh, tid, row_of);
+      vs.template load<false>(Vh, tid, row_of);
     } else {
       const int64_t r0 = (int64_t)tab[t] * kBN;
       auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
-      ks.template load<true, true>(Kh, tid, row_of);
-      vs.template load<true, false>(Vh, tid, row_of);
+      ks.template load<true>(Kh, tid, row_of);
+      vs.template load<false>(Vh, tid, row_of);
     }
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
-    ks.template store<true, true>(b, b + 2 * RM<D>::kBytes, tid);
-    vs.template store<true, false>(b + RM<D>::kBytes, nullptr, tid);
+    ks.template store<true>(b, b + 2 * RM<D>::kBytes, tid);
+    vs.template store<false>(b + RM<D>::kBytes, nullptr, tid);
   };
 
   f32x16_t dq[ND];
@@ -258,13 +304,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p) {
     const unsigned char* vrm = krm + RM<D>::kBytes;
     const unsigned char* ktr = krm + 2 * RM<D>::kBytes;
 
+    // four independent accumulator chains (s, dp of both key halves), so no
+    // MFMA waits on the one before it
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       s[h] = zero16();
       dp[h] = zero16();
+    }
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
         const int off = (32 * h + l32) * RM<D>::kStride + (16 * kk + 8 * hi) * 2;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krm + off);
         s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[h], 0, 0, 0);
@@ -299,8 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p) {
 #undef ISA_DS
 #define ISA_DQ(V, C)                                                                    \
   _Pragma("unroll") for (int j = 0; j < ND; ++j) {                                      \
-    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(                              \
-        ktr + (32 * j + l32) * TR<D>::kStride + (16 * (C) + 8 * hi) * 2);               \
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktr + trr.off(j, C));         \
     dq[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, V, dq[j], 0, 0, 0);              \
   }
     ISA_DQ(ds0, 0)
@@ -363,6 +413,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p)
     kreg[kk] = *reinterpret_cast<const bf16x8_t*>(Kh + krow * D + 16 * kk + 8 * hi);
     vreg[kk] = *reinterpret_cast<const bf16x8_t*>(Vh + krow * D + 16 * kk + 8 * hi);
   }
+  // retire these loads here (see the dQ kernel)
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm("" : "+v"(kreg[kk]), "+v"(vreg[kk]));
 
   const bf16_bits* Qh = p.q + bh * p.q_head_stride;
   const bf16_bits* dOh = p.dout + bh * p.q_head_stride;
@@ -372,12 +425,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p)
   TileStager<D> qs, os;
   qs.init(tid);
   os.init(tid);
+  TrReader<D> trr;
+  trr.init(l32, hi);
   float st_lse = 0.0f;  // thread tid < 64: lse2 of query row tid; 64..127: delta
   auto load = [&](int e) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)qtab[e] * kBlock;
     auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
-    qs.template load<true, true>(Qh, tid, row_of);
-    os.template load<true, true>(dOh, tid, row_of);
+    qs.template load<true>(Qh, tid, row_of);
+    os.template load<true>(dOh, tid, row_of);
     if (tid < kBN)
       st_lse = (lseh[r0 + tid] - p.lse_offset) * 1.4426950408889634f;
     else if (tid < 2 * kBN)
@@ -385,8 +440,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p)
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
-    qs.template store<true, true>(b, b + 2 * RM<D>::kBytes, tid);
-    os.template store<true, true>(b + RM<D>::kBytes, b + 2 * RM<D>::kBytes + TR<D>::kBytes, tid);
+    qs.template store<true>(b, b + 2 * RM<D>::kBytes, tid);
+    os.template store<true>(b + RM<D>::kBytes, b + 2 * RM<D>::kBytes + TR<D>::kBytes, tid);
     if (tid < 2 * kBN)
       reinterpret_cast<float*>(b + 2 * RM<D>::kBytes + 2 * TR<D>::kBytes)[tid] = st_lse;
   };
@@ -420,8 +475,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p)
     for (int h = 0; h < 2; ++h) {
       s[h] = zero16();
       dp[h] = zero16();
+    }
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // four independent accumulator chains
         const int off = (32 * h + l32) * RM<D>::kStride + (16 * kk + 8 * hi) * 2;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qrm + off);
         s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[kk], s[h], 0, 0, 0);
@@ -461,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p)
     // dV^T += dO^T P, dK^T += Q^T dS (contraction over the 64 queries)
 #define ISA_KV(PV, DV, C)                                                               \
   _Pragma("unroll") for (int j = 0; j < ND; ++j) {                                      \
-    const int off = (32 * j + l32) * TR<D>::kStride + (16 * (C) + 8 * hi) * 2;          \
+    const int off = trr.off(j, C);                                                      \
     const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(otr + off);                   \
     dv[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, PV, dv[j], 0, 0, 0);             \
     const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(qtr + off);                   \
