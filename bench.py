@@ -32,8 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # the kernel source it was measured on; reported only while that source is
 # unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_exact_isa_bf16_N32768_hbm_traffic.txt")
-EXACT_KERNEL_SRC = os.path.join(ROOT, "sparse_attention_context_block_amd", "csrc",
-                                "isa_attn_pp.hip")
+# (the kernel's file and the internal header it includes)
+EXACT_KERNEL_SRC = tuple(os.path.join(ROOT, "sparse_attention_context_block_amd", "csrc", f)
+                         for f in ("isa_attn_pp.hip", "isa_internal.h"))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -97,7 +98,10 @@ def cpu_baseline(inp, c, n_heads):
 def kernel_source_sha256():
     import hashlib
 
-    return hashlib.sha256(open(EXACT_KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in EXACT_KERNEL_SRC:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():

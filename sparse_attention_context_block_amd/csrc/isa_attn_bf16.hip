@@ -37,12 +37,6 @@ constexpr int kThreads = 256;
 constexpr int kBN = 64;          // keys per tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-__device__ inline uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
-  // select the low or high bf16 of two words into one word
-  return high ? ((lo_word >> 16) | (hi_word & 0xffff0000u))
-              : ((lo_word & 0xffffu) | (hi_word << 16));
-}
-
 template <int D>
 struct Smem {
   static constexpr int kKStride = D * 2 + 16;    // bytes per K row (padded)

@@ -71,11 +71,6 @@ constexpr int kBN = 64;
 // native vector (not HIP's uint4 struct) so staging registers never leave VGPRs
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
-  return high ? ((lo_word >> 16) | (hi_word & 0xffff0000u))
-              : ((lo_word & 0xffffu) | (hi_word << 16));
-}
-
 // LDS tile of 64 rows x D bf16, row-major with a 16-byte row pad.
 template <int D>
 struct RM {

@@ -27,11 +27,6 @@ constexpr int kBN = 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
-  return high ? ((lo_word >> 16) | (hi_word & 0xffff0000u))
-              : ((lo_word & 0xffffu) | (hi_word << 16));
-}
-
 template <int D>
 struct FlatSmem {
   static constexpr int kKStride = D * 2 + 16;

@@ -37,11 +37,6 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 // Workgroup barrier between phases.
 __device__ __forceinline__ void phase_barrier() { __syncthreads(); }
 
-__device__ inline uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
-  return high ? ((lo_word >> 16) | (hi_word & 0xffff0000u))
-              : ((lo_word & 0xffffu) | (hi_word << 16));
-}
-
 template <int D>
 struct Lds {
   static constexpr int kKStride = D * 2 + 16;    // bytes per K row (padded)

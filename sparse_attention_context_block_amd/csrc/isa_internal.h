@@ -14,6 +14,13 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
+// Two bf16 from two words: the low halves (high = false) or the high halves
+// (high = true) of lo_word and hi_word, lo_word's in the low half of the
+// result.  One byte permute (v_perm_b32).
+__device__ __forceinline__ uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bool high) {
+  return __builtin_amdgcn_perm(hi_word, lo_word, high ? 0x07060302u : 0x05040100u);
+}
+
 // Block length the device kernels are built for (tokens per pooled block;
 // also the key-tile height of the attention kernels).
 constexpr int kBlock = 64;
