@@ -20,6 +20,9 @@ Pages cited (by title and section):
              attention, pooling attention), 3 In-Context Sparse Attention
              (pre-selection, Taylor sparse attention, grouped computation).
 
+The decoupled rotary embedding ([notes] "training strategy") is in
+``isa_oracle_rope`` with its readings R22-R24.
+
 Every reading of a point the pages leave open is listed in ``isa_oracle``'s
 module docstring.
 """
@@ -46,3 +49,12 @@ from .isa_oracle import (  # noqa: F401
     dense_ref,
 )
 from .isa_oracle_bwd import isa_ref_bwd, dense_ref_bwd  # noqa: F401
+from .isa_oracle_rope import (  # noqa: F401
+    round_to_bf16,
+    round_to_dtype,
+    rope_positions,
+    rope_inv_freq,
+    rotate_pairs,
+    decoupled_rope,
+    isa_ref_rope,
+)

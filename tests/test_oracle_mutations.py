@@ -54,17 +54,38 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_reject_planted_mistake(tmp_path, name, old, new):
-    src = open(os.path.join(ROOT, "oracle", "isa_oracle.py")).read()
+# mistakes in the rotary embedding (oracle/isa_oracle_rope.py)
+ROPE_MUTATIONS = [
+    ("rope turns the other way", "out[..., 0::2] = x * c - y * s", "out[..., 0::2] = x * c + y * s"),
+    ("rope context positions continue the source",
+     "np.concatenate([np.arange(L_src), np.arange(L_ctx)])",
+     "np.concatenate([np.arange(L_src), np.arange(L_src, L_src + L_ctx)])"),
+    ("rope pairs the two halves instead of neighbours", "x, y = X[..., 0::2], X[..., 1::2]",
+     "h = X.shape[-1] // 2\n    x, y = X[..., :h], X[..., h:]"),
+    ("rope frequency exponent halved", "return np.power(float(base), -2.0 * i / D)",
+     "return np.power(float(base), -i / D)"),
+    ("bf16 rounding through fp32", "    if dtype == \"bf16\":\n        return round_to_bf16(x)",
+     "    if dtype == \"bf16\":\n        return round_to_bf16(np.asarray(x).astype(np.float32)"
+     ".astype(np.float64))"),
+    ("bf16 rounding ties away from zero", "return np.ldexp(np.rint(m * 256.0), e - 8)",
+     "return np.ldexp(np.trunc(m * 256.0 + np.copysign(0.5, m)), e - 8)"),
+]
+
+ALL = [(n, o, w, "isa_oracle.py") for n, o, w in MUTATIONS] + \
+      [(n, o, w, "isa_oracle_rope.py") for n, o, w in ROPE_MUTATIONS]
+
+
+@pytest.mark.parametrize("name,old,new,fname", ALL, ids=[m[0] for m in ALL])
+def test_pins_reject_planted_mistake(tmp_path, name, old, new, fname):
+    src = open(os.path.join(ROOT, "oracle", fname)).read()
     assert src.count(old) == 1, f"mutation anchor missing: {old!r}"
     for d in ("oracle", "synth", "tests"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
     shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
-    (tmp_path / "oracle" / "isa_oracle.py").write_text(src.replace(old, new))
+    (tmp_path / "oracle" / fname).write_text(src.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_bwd_pins.py",
-                        "tests/test_oracle_ns_pins.py"],
+                        "tests/test_oracle_ns_pins.py", "tests/test_oracle_rope_pins.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"no pin caught the planted mistake: {name}\n{r.stdout[-2000:]}"
