@@ -11,10 +11,10 @@ Prints ONE JSON line with the latency, the dense-equivalent TFLOP/s
 (4 B H N^2 D / latency), the per-stage times (HIP events recorded between the
 stages on the launch stream, inside the timed region), the roofline of the
 dominant kernel (the exact path), the library's own dense attention on the same
-input, and the fp64 CPU oracle timed on a bounded sample.  Two extra sections
-time the same workload with the block mask inside flat query blocks
-(alpha_ns, default 0.0625) and the decision-frozen backward of the B=2
-N=16384 workload.
+input, and the fp64 CPU oracle timed on a bounded sample.  Extra sections time
+the same workload with the block mask inside flat query blocks (alpha_ns,
+default 0.0625) and with the decoupled rotary embedding (base 10000), and the
+decision-frozen backward of the B=2 N=16384 workload.
 """
 
 import argparse
@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--mask-alpha-ns", type=float, default=0.0625,
                     help="also time the forward with this block-mask ratio (0 = skip)")
     ap.add_argument("--mask-steps", type=int, default=10)
+    ap.add_argument("--rope-base", type=float, default=10000.0,
+                    help="also time the forward with the decoupled rotary embedding (0 = skip)")
+    ap.add_argument("--rope-steps", type=int, default=10)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the workload line: ISA vs dense over N = 5K..64K")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -205,13 +208,13 @@ def bench_backward(args, isa, torch, dev):
             "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12}
 
 
-def bench_block_mask(args, isa, torch, q, k, v, c):
-    """The same workload with the block mask inside flat query blocks
-    (alpha_ns > 0): latency, stage times and the flat-path kernel's rate."""
+def _time_variant(isa, torch, q, k, v, c, steps, alpha_ns=0.0, rope_base=0.0):
+    """Time the workload's forward under another plan (3 untimed calls, then
+    `steps` timed ones with per-stage events).  Returns (ms, stage_ms, info)."""
     B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
     N = L_src + L_ctx
-    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"],
-                               args.mask_alpha_ns)
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"], alpha_ns,
+                               rope_base=rope_base)
     info = plan.info
     ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
@@ -219,21 +222,49 @@ def bench_block_mask(args, isa, torch, q, k, v, c):
     for _ in range(3):
         isa.isa_forward(plan, q, k, v, o, lse, workspace=ws)
     n_ev = isa.ISA_PROFILE_STAGES + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-              for _ in range(args.mask_steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     for evs in events:
         for ev in evs:
             ev.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.mask_steps):
+    for i in range(steps):
         isa.isa_forward(plan, q, k, v, o, lse, workspace=ws, events=events[i])
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.mask_steps
+    ms = start.elapsed_time(end) / steps
     stage_ms = {name: float(np.mean([evs[j].elapsed_time(evs[j + 1]) for evs in events]))
                 for j, name in enumerate(isa.STAGE_NAMES)}
+    return ms, stage_ms, info
+
+
+def bench_rope(args, isa, torch, q, k, v, c):
+    """The same workload with the decoupled rotary embedding: latency, stage
+    times, and the pooling kernel's rate now that it also rotates Q and K
+    (reads Q, K, V and writes the rotated Q, K, plus the pooled outputs)."""
+    B, H, N, D = c["B"], c["H"], c["L_src"] + c["L_ctx"], c["D"]
+    ms, stage_ms, info = _time_variant(isa, torch, q, k, v, c, args.rope_steps,
+                                       rope_base=args.rope_base)
+    pool_bytes = 5.0 * B * H * N * D * 2 + B * H * info["n_q_blocks"] * D * (8 + 8 + 2 + 2)
+    p_ms = stage_ms["pool"]
+    _log(f"rope base {args.rope_base}: ISA forward {ms:.3f} ms; pool + rotation {p_ms:.3f} ms")
+    return {"rope_base": args.rope_base, "latency_ms": ms,
+            "dense_equiv_tflops": 4.0 * B * H * N * N * D / (ms * 1e-3) / 1e12,
+            "stages_ms": stage_ms,
+            "pool_rope": {"kernel": "pool_kernel<unsigned short, 128, true>", "ms": p_ms,
+                          "algorithmic_bytes": pool_bytes,
+                          "GB/s": pool_bytes / (p_ms * 1e-3) / 1e9,
+                          "hbm_frac": pool_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
+
+def bench_block_mask(args, isa, torch, q, k, v, c):
+    """The same workload with the block mask inside flat query blocks
+    (alpha_ns > 0): latency, stage times and the flat-path kernel's rate."""
+    B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
+    N = L_src + L_ctx
+    ms, stage_ms, info = _time_variant(isa, torch, q, k, v, c, args.mask_steps,
+                                       alpha_ns=args.mask_alpha_ns)
     # flat rows: n_ns * b exact keys plus n_kv - n_ns representative rows each
     flat_keys = info["n_ns"] * b + info["n_kv_blocks"] - info["n_ns"]
     flat_flops = 4.0 * B * H * info["n_flat"] * b * flat_keys * D
@@ -407,6 +438,9 @@ def main():
     block_mask = None
     if args.mask_alpha_ns > 0:
         block_mask = bench_block_mask(args, isa, torch, q, k, v, c)
+    rope = None
+    if args.rope_base > 0:
+        rope = bench_rope(args, isa, torch, q, k, v, c)
 
     dense = None
     if not args.no_dense:
@@ -470,6 +504,7 @@ def main():
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
         "roofline": roofline,
         "block_mask": block_mask,
+        "rope": rope,
         "backward": backward,
         "cpu_baseline": cpu,
     }

@@ -65,6 +65,12 @@ typedef struct {
                          /* ceil(alpha_ns * n_kv) K_new blocks with the largest coarse */
                          /* score are computed exactly ([notes] key design 2 mask)    */
   isa_dtype_t dtype;     /* storage and input type of Q, K, V, O                      */
+  double rope_base;      /* > 0: decoupled rotary embedding of Q and K before every  */
+                         /* step ([notes] training strategy: source and context      */
+                         /* positions each start at 0).  Pair (2i, 2i+1) of a token  */
+                         /* at position pos turns by pos * rope_base^(-2i/D)          */
+                         /* (RoFormer's rotation); the rotated values are rounded     */
+                         /* once, to nearest even, to dtype.  0: no embedding.        */
 } isa_plan_desc_t;
 
 typedef struct isa_plan_s* isa_plan_t;
@@ -102,7 +108,8 @@ typedef struct {
 /* Validate a description and derive the sizes; host only, never calls HIP.
  * The plan is immutable and may be shared across threads and streams.
  * Errors: ISA_ERR_INVALID_ARG (null out/desc, B/H/D/block < 1 or negative,
- * L_src < 1, L_ctx < 0, a ratio outside [0, 1] or NaN),
+ * L_src < 1, L_ctx < 0, a ratio outside [0, 1] or NaN, rope_base negative,
+ * infinite or NaN),
  * ISA_ERR_UNSUPPORTED (block != 64, D not 64/128, unknown dtype). */
 isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc);
 
@@ -127,6 +134,8 @@ isa_status_t isa_plan_destroy(isa_plan_t plan);
  *      to the smaller K_new position) enter token by token instead, in the
  *      same softmax;
  *   5. O = O / l (bf16 round-to-nearest-even for BF16), lse = m + ln l.
+ * With rope_base > 0, every step sees the rotated Q and K (written into the
+ * workspace by the pooling kernel).
  * Q, K, V, O: [B, H, N, D] of `dtype`.  lse: [B, H, N] float, may be NULL.
  * aux: optional decision outputs (see isa_aux_t), may be NULL.
  * workspace: device memory of at least info.workspace_bytes.
@@ -181,8 +190,8 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * [B, H, N] float from the forward; aux: sel, flat and sharp from the
  * forward (required).  workspace: at least isa_backward_workspace_bytes().
  * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, a plan with
- * n_ns > 0, or L_src / L_ctx not a multiple of 64), ISA_ERR_WORKSPACE,
- * ISA_ERR_HIP. */
+ * n_ns > 0 or rope_base > 0, or L_src / L_ctx not a multiple of 64),
+ * ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

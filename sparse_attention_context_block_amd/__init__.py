@@ -43,7 +43,8 @@ class isa_plan_desc_t(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L_src", ctypes.c_int32),
                 ("L_ctx", ctypes.c_int32), ("D", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("alpha_s", ctypes.c_double), ("alpha_f", ctypes.c_double),
-                ("alpha_ns", ctypes.c_double), ("dtype", ctypes.c_int)]
+                ("alpha_ns", ctypes.c_double), ("dtype", ctypes.c_int),
+                ("rope_base", ctypes.c_double)]
 
 
 class isa_plan_info_t(ctypes.Structure):
@@ -121,9 +122,10 @@ class Plan:
 
 
 def isa_plan_create(B, H, L_src, L_ctx, D, block=64, alpha_s=0.25, alpha_f=0.5, alpha_ns=0.0,
-                    dtype=torch.bfloat16):
+                    dtype=torch.bfloat16, rope_base=0.0):
     desc = isa_plan_desc_t(B, H, L_src, L_ctx, D, block, alpha_s, alpha_f, alpha_ns,
-                           _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+                           _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+                           rope_base)
     h = ctypes.c_void_p()
     _check(_lib().isa_plan_create(ctypes.byref(h), ctypes.byref(desc)), "isa_plan_create")
     return Plan(h, desc)

@@ -14,6 +14,7 @@ using namespace isa;
 struct WorkspaceLayout {
   size_t qc, kc, kc_lp, vc_lp, rowmax, rowsum, sharpness, ctx_score, sel, flat, sharp, kv_tab;
   size_t logits, ns;  // only with n_ns > 0 and n_flat > 0
+  size_t qr, kr;      // only with the rotary embedding: rotated Q, K
   size_t total;
 };
 
@@ -25,6 +26,8 @@ struct isa_plan_s {
   int32_t BH;
   BlockGrid grid;   // token layout of the blocks
   bool aligned;     // L_src and L_ctx are multiples of the block length
+  bool rope;        // decoupled rotary embedding of Q and K
+  RopeFreq freq;    // its pair frequencies base^(-2i/D)
 };
 
 namespace {
@@ -93,6 +96,7 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
     return ISA_ERR_INVALID_ARG;
   if (!ratio_ok(d.alpha_s) || !ratio_ok(d.alpha_f) || !ratio_ok(d.alpha_ns))
     return ISA_ERR_INVALID_ARG;
+  if (!(d.rope_base >= 0.0) || isinf(d.rope_base)) return ISA_ERR_INVALID_ARG;
   if (d.dtype != ISA_DTYPE_BF16 && d.dtype != ISA_DTYPE_FP32) return ISA_ERR_INVALID_ARG;
   if ((int64_t)d.L_src + d.L_ctx > INT32_MAX / 2) return ISA_ERR_UNSUPPORTED;
   if (d.block != kBlock || (d.D != 64 && d.D != 128)) return ISA_ERR_UNSUPPORTED;
@@ -106,6 +110,10 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   p->BH = (int32_t)BH;
   p->N = (int64_t)d.L_src + d.L_ctx;
   p->aligned = d.L_src % kBlock == 0 && d.L_ctx % kBlock == 0;
+  p->rope = d.rope_base > 0.0;
+  // pair i of D/2 turns by pos * base^(-2i/D) (the exponent as -2 i / D in double)
+  for (int i = 0; p->rope && i < d.D / 2; ++i)
+    p->freq.inv_freq[i] = pow(d.rope_base, -2.0 * i / d.D);
   isa_plan_info_t& in = p->info;
   in.n_src_blocks = (d.L_src + d.block - 1) / d.block;
   in.n_ctx_blocks = (d.L_ctx + d.block - 1) / d.block;
@@ -147,6 +155,9 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   const bool masked = in.n_ns > 0 && in.n_flat > 0;
   w.logits = masked ? take((size_t)BH * in.n_q_blocks * in.n_q_blocks * sizeof(double)) : 0;
   w.ns = masked ? take((size_t)BH * in.n_flat * in.n_ns * sizeof(int32_t)) : 0;
+  const size_t tokens = (size_t)BH * p->N * d.D * elt_size(d.dtype);
+  w.qr = p->rope ? take(tokens) : 0;
+  w.kr = p->rope ? take(tokens) : 0;
   w.total = off;
   in.workspace_bytes = off;
   *out = p;
@@ -214,10 +225,18 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
     if ((st = record(events, (i), s)) != ISA_OK) return st; \
   } while (0)
   ISA_STAGE(0);
+  // 0. with the decoupled rotary embedding, the pooling kernel rotates Q and K
+  //    into the workspace and every later step reads the rotated copies
+  void* qr = plan->rope ? w + L.qr : nullptr;
+  void* kr = plan->rope ? w + L.kr : nullptr;
   // 1. pooling attention: block means, then the coarse map's row statistics
   //    and sharpness, and the context column means (all fp64)
   ISA_LAUNCH(launch_pool(Q, K, V, d.dtype, BH, N, D, d.L_src, n_src, n_q, d.block, qc, kc,
-                         kc_lp, vc_lp, s));
+                         kc_lp, vc_lp, qr, kr, plan->rope ? &plan->freq : nullptr, s));
+  if (plan->rope) {
+    Q = qr;
+    K = kr;
+  }
   ISA_STAGE(1);
   ISA_LAUNCH(launch_coarse_rowstats(qc, kc, BH, n_q, D, rowmax, rowsum, sharpness, logits, s));
   ISA_STAGE(2);
@@ -427,6 +446,7 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
   if (plan->info.n_ns > 0 && plan->info.n_flat > 0) return ISA_ERR_UNSUPPORTED;
   if (!plan->aligned) return ISA_ERR_UNSUPPORTED;
+  if (plan->rope) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);

@@ -644,8 +644,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       b += red[1][i][tid];
     }
     const int64_t o = (bh * n_kv + t) * (int64_t)D + tid;
-    kc[o] = __builtin_bit_cast(bf16_bits, (__bf16)(float)(a * (1.0 / kBlock)));
-    vc[o] = __builtin_bit_cast(bf16_bits, (__bf16)(float)(b * (1.0 / kBlock)));
+    kc[o] = (bf16_bits)bf16_bits_rne(a * (1.0 / kBlock));  // as the forward's pooling rounds
+    vc[o] = (bf16_bits)bf16_bits_rne(b * (1.0 / kBlock));
   }
 }
 

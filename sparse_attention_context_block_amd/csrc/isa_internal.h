@@ -21,6 +21,16 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo_word, uint32_t hi_word, bo
   return __builtin_amdgcn_perm(hi_word, lo_word, high ? 0x07060302u : 0x05040100u);
 }
 
+// fp64 -> bf16 bits, round to nearest even, in one rounding: truncate to fp32
+// and keep the lost part as a sticky bit (round to odd, exact for any later
+// rounding to 22 or fewer significant bits), then round the fp32 to bf16.
+__device__ __forceinline__ uint32_t bf16_bits_rne(double x) {
+  const float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x) u |= 1u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Block length the device kernels are built for (tokens per pooled block;
 // also the key-tile height of the attention kernels).
 constexpr int kBlock = 64;
@@ -124,9 +134,18 @@ hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int
                             int BH, int n_q, int n_flat, int n_kv, int n_ns, int32_t* ns,
                             hipStream_t stream);
 
+// Frequencies of the rotary embedding, base^(-2i/D) for the D/2 pairs
+// (computed on the host, passed by value).
+struct RopeFreq {
+  double inv_freq[64];
+};
+
+// Block means of Q, K, V; with rope (non-null) Q and K are first rotated and
+// the rotated rows written to qr, kr.
 hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t dtype,
                        int BH, int N, int D, int L_src, int n_src, int n_q, int block,
-                       double* qc, double* kc, void* kc_lp, void* vc_lp, hipStream_t stream);
+                       double* qc, double* kc, void* kc_lp, void* vc_lp, void* qr, void* kr,
+                       const RopeFreq* rope, hipStream_t stream);
 
 hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
                                   double* rowmax, double* rowsum, double* sharpness,

@@ -1,10 +1,19 @@
 // Block-mean pooling of Q, K and V: the block representatives of pooling
 // attention ([summary] 2 "Pooling Attention"; [notes] key design 2 calls K^c
 // and V^c the representative value of a block).  One workgroup per (block,
-// head); fp64 accumulation, so the fp64 means of bf16 inputs are exact.
+// head), or per (block, group of 8 heads) with the rotation below; fp64
+// accumulation, so the fp64 means of bf16 inputs are exact.
 //
 // Outputs: qc, kc [BH][n_q][D] fp64 (the coarse stage runs in fp64), and
 // kc_lp, vc_lp [BH][n_q][D] in the input dtype (operands of the Taylor path).
+//
+// With the decoupled rotary embedding ([notes] training strategy: source and
+// context positions each start at 0) the kernel also rotates Q and K on the
+// way: pair (2i, 2i+1) of the token at position pos turns by
+// pos * base^(-2i/D) (RoFormer's rotation), computed in fp64 and rounded once,
+// to nearest even, to the input dtype.  The rotated rows go to qr, kr (every
+// later step reads them) and the block means are taken of the rotated,
+// rounded values.
 #include "isa_internal.h"
 
 namespace isa {
@@ -21,9 +30,19 @@ template <> struct Elt<bf16_bits> {
       out[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
     }
   }
-  __device__ static bf16_bits from_double(double x) {
-    return __builtin_bit_cast(bf16_bits, (__bf16)(float)x);
+  // round x in place to bf16 values and pack them into a chunk
+  __device__ static uint4 round_pack(double* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = bf16_bits_rne(x[2 * i]), hi = bf16_bits_rne(x[2 * i + 1]);
+      x[2 * i] = (double)__uint_as_float(lo << 16);
+      x[2 * i + 1] = (double)__uint_as_float(hi << 16);
+      w[i] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
   }
+  __device__ static bf16_bits from_double(double x) { return (bf16_bits)bf16_bits_rne(x); }
 };
 template <> struct Elt<float> {
   static constexpr int kPerChunk = 4;
@@ -33,23 +52,47 @@ template <> struct Elt<float> {
     out[2] = (double)__uint_as_float(u.z);
     out[3] = (double)__uint_as_float(u.w);
   }
+  __device__ static uint4 round_pack(double* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = (float)x[i];
+      x[i] = (double)f;
+      w[i] = __float_as_uint(f);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
   __device__ static float from_double(double x) { return (float)x; }
 };
 
-constexpr int kThreads = 256;
+// (x, y) turned by the angle with cosine c and sine s, each product and sum
+// rounded on its own (no fused multiply-add), as the textbook formula reads.
+__device__ inline void rotate_pair(double& x, double& y, double c, double s) {
+#pragma clang fp contract(off)
+  const double xc = x * c, ys = y * s, xs = x * s, yc = y * c;
+  x = xc - ys;
+  y = xs + yc;
+}
 
-template <typename T, int D>
+constexpr int kThreads = 256;
+constexpr int kRopeHeads = 8;  // heads per workgroup when the kernel also rotates
+
+template <typename T, int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void pool_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int N, int L_src,
-    int n_src, int n_q, int block, double* __restrict__ qc, double* __restrict__ kc,
-    T* __restrict__ kc_lp, T* __restrict__ vc_lp) {
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int BH, int N,
+    int L_src, int n_src, int n_q, int block, double* __restrict__ qc, double* __restrict__ kc,
+    T* __restrict__ kc_lp, T* __restrict__ vc_lp, T* __restrict__ qr, T* __restrict__ kr,
+    RopeFreq rope) {
   constexpr int EPC = Elt<T>::kPerChunk;
   constexpr int CH = D / EPC;          // 16-byte chunks per row
   constexpr int RP = kThreads / CH;    // rows covered per pass
+  constexpr int JMAX = (kBlock + RP - 1) / RP;  // rows per thread of a block (rotation)
+  // heads per workgroup: with the rotation, one block's angles serve this many heads
+  constexpr int kHeads = kRope ? kRopeHeads : 1;
   __shared__ double red[3][RP][D];
 
   const int blk = blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  const int64_t bh0 = (int64_t)blockIdx.y * kHeads;
   const int tid = threadIdx.x;
   // block grid: source blocks from 0, context blocks from L_src, each segment
   // cut from its own start (the last block of a segment may be partial)
@@ -65,63 +108,110 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
   const int c = tid % CH;
   const int r0 = tid / CH;
 
-  double acc[3][EPC];
+  // rotation angles of this thread's rows (r0 + RP j) and pairs (dims
+  // c EPC + 2 p, c EPC + 2 p + 1), computed once for all heads of the group
+  double cs[kRope ? JMAX : 1][EPC / 2], sn[kRope ? JMAX : 1][EPC / 2];
+  if constexpr (kRope) {
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+    for (int j = 0; j < JMAX; ++j) {
+      const int t = start + r0 + RP * j;
+      const double pos = (double)(t < L_src ? t : t - L_src);  // positions restart at the context
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[t][e] = 0.0;
-
-  const int64_t base = (bh * N + start) * (int64_t)D + c * EPC;
-  for (int r = r0; r < rows; r += RP) {
-    const int64_t off = base + (int64_t)r * D;
-    const uint4 uq = *reinterpret_cast<const uint4*>(Q + off);
-    const uint4 uk = *reinterpret_cast<const uint4*>(K + off);
-    const uint4 uv = *reinterpret_cast<const uint4*>(V + off);
-    double x[EPC];
-    Elt<T>::unpack(uq, x);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[0][e] += x[e];
-    Elt<T>::unpack(uk, x);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[1][e] += x[e];
-    Elt<T>::unpack(uv, x);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[2][e] += x[e];
-  }
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) red[t][r0][c * EPC + e] = acc[t][e];
-  __syncthreads();
-
-  const int64_t out = (bh * n_q + blk) * (int64_t)D;
-  for (int idx = tid; idx < 3 * D; idx += kThreads) {
-    const int t = idx / D, d = idx % D;
-    double s = 0.0;
-#pragma unroll
-    for (int g = 0; g < RP; ++g) s += red[t][g][d];  // fixed order
-    const double mean = s / (double)rows;
-    if (t == 0) {
-      qc[out + d] = mean;
-    } else if (t == 1) {
-      kc[out + d] = mean;
-      kc_lp[out + d] = Elt<T>::from_double(mean);
-    } else {
-      vc_lp[out + d] = Elt<T>::from_double(mean);
+      for (int pr = 0; pr < EPC / 2; ++pr)
+        sincos(pos * rope.inv_freq[c * (EPC / 2) + pr], &sn[j][pr], &cs[j][pr]);
     }
+  }
+
+  for (int hh = 0; hh < kHeads; ++hh) {
+    const int64_t bh = bh0 + hh;
+    if (bh >= BH) break;  // uniform across the workgroup
+    double acc[3][EPC];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[t][e] = 0.0;
+
+    const int64_t base = (bh * N + start) * (int64_t)D + c * EPC;
+    auto row = [&](int r, int j) __attribute__((always_inline)) {
+      const int64_t off = base + (int64_t)r * D;
+      const uint4 uq = *reinterpret_cast<const uint4*>(Q + off);
+      const uint4 uk = *reinterpret_cast<const uint4*>(K + off);
+      const uint4 uv = *reinterpret_cast<const uint4*>(V + off);
+      double x[EPC], y[EPC];
+      Elt<T>::unpack(uq, x);
+      Elt<T>::unpack(uk, y);
+      if constexpr (kRope) {
+#pragma unroll
+        for (int pr = 0; pr < EPC / 2; ++pr) {
+          rotate_pair(x[2 * pr], x[2 * pr + 1], cs[j][pr], sn[j][pr]);
+          rotate_pair(y[2 * pr], y[2 * pr + 1], cs[j][pr], sn[j][pr]);
+        }
+        *reinterpret_cast<uint4*>(qr + off) = Elt<T>::round_pack(x);
+        *reinterpret_cast<uint4*>(kr + off) = Elt<T>::round_pack(y);
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[0][e] += x[e];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[1][e] += y[e];
+      Elt<T>::unpack(uv, x);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[2][e] += x[e];
+    };
+    if constexpr (kRope) {
+      // the launcher guarantees block <= kBlock, so JMAX passes cover a block
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j)
+        if (r0 + RP * j < rows) row(r0 + RP * j, j);
+    } else {
+      for (int r = r0; r < rows; r += RP) row(r, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) red[t][r0][c * EPC + e] = acc[t][e];
+    __syncthreads();
+
+    const int64_t out = (bh * n_q + blk) * (int64_t)D;
+    for (int idx = tid; idx < 3 * D; idx += kThreads) {
+      const int t = idx / D, d = idx % D;
+      double s = 0.0;
+#pragma unroll
+      for (int g = 0; g < RP; ++g) s += red[t][g][d];  // fixed order
+      const double mean = s / (double)rows;
+      if (t == 0) {
+        qc[out + d] = mean;
+      } else if (t == 1) {
+        kc[out + d] = mean;
+        kc_lp[out + d] = Elt<T>::from_double(mean);
+      } else {
+        vc_lp[out + d] = Elt<T>::from_double(mean);
+      }
+    }
+    __syncthreads();  // red is reused by the next head
   }
 }
 
 template <typename T, int D>
-hipError_t launch_typed(const void* Q, const void* K, const void* V, int BH, int N, int D_,
+hipError_t launch_typed(const void* Q, const void* K, const void* V, int BH, int N,
                         int L_src, int n_src, int n_q, int block, double* qc, double* kc,
-                        void* kc_lp, void* vc_lp, hipStream_t stream) {
-  (void)D_;
-  dim3 grid(n_q, BH);
-  hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(Q), static_cast<const T*>(K),
-                     static_cast<const T*>(V), N, L_src, n_src, n_q, block, qc, kc,
-                     static_cast<T*>(kc_lp), static_cast<T*>(vc_lp));
+                        void* kc_lp, void* vc_lp, void* qr, void* kr, const RopeFreq* rope,
+                        hipStream_t stream) {
+  if (rope) {
+    if (block > kBlock) return hipErrorInvalidValue;  // the angle cache covers kBlock rows
+    dim3 grid(n_q, (BH + kRopeHeads - 1) / kRopeHeads);
+    hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(Q), static_cast<const T*>(K),
+                       static_cast<const T*>(V), BH, N, L_src, n_src, n_q, block, qc, kc,
+                       static_cast<T*>(kc_lp), static_cast<T*>(vc_lp), static_cast<T*>(qr),
+                       static_cast<T*>(kr), *rope);
+  } else {
+    dim3 grid(n_q, BH);
+    hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(Q), static_cast<const T*>(K),
+                       static_cast<const T*>(V), BH, N, L_src, n_src, n_q, block, qc, kc,
+                       static_cast<T*>(kc_lp), static_cast<T*>(vc_lp), nullptr, nullptr,
+                       RopeFreq{});
+  }
   return hipGetLastError();
 }
 
@@ -129,20 +219,22 @@ hipError_t launch_typed(const void* Q, const void* K, const void* V, int BH, int
 
 hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t dtype, int BH,
                        int N, int D, int L_src, int n_src, int n_q, int block, double* qc,
-                       double* kc, void* kc_lp, void* vc_lp, hipStream_t stream) {
+                       double* kc, void* kc_lp, void* vc_lp, void* qr, void* kr,
+                       const RopeFreq* rope, hipStream_t stream) {
   if (BH == 0 || n_q == 0) return hipSuccess;
+  if (rope && (!qr || !kr)) return hipErrorInvalidValue;
   if (dtype == ISA_DTYPE_BF16) {
     if (D == 128)
-      return launch_typed<bf16_bits, 128>(Q, K, V, BH, N, D, L_src, n_src, n_q, block, qc, kc,
-                                          kc_lp, vc_lp, stream);
-    return launch_typed<bf16_bits, 64>(Q, K, V, BH, N, D, L_src, n_src, n_q, block, qc, kc,
-                                       kc_lp, vc_lp, stream);
+      return launch_typed<bf16_bits, 128>(Q, K, V, BH, N, L_src, n_src, n_q, block, qc, kc,
+                                          kc_lp, vc_lp, qr, kr, rope, stream);
+    return launch_typed<bf16_bits, 64>(Q, K, V, BH, N, L_src, n_src, n_q, block, qc, kc,
+                                       kc_lp, vc_lp, qr, kr, rope, stream);
   }
   if (D == 128)
-    return launch_typed<float, 128>(Q, K, V, BH, N, D, L_src, n_src, n_q, block, qc, kc, kc_lp,
-                                    vc_lp, stream);
-  return launch_typed<float, 64>(Q, K, V, BH, N, D, L_src, n_src, n_q, block, qc, kc, kc_lp,
-                                 vc_lp, stream);
+    return launch_typed<float, 128>(Q, K, V, BH, N, L_src, n_src, n_q, block, qc, kc, kc_lp,
+                                    vc_lp, qr, kr, rope, stream);
+  return launch_typed<float, 64>(Q, K, V, BH, N, L_src, n_src, n_q, block, qc, kc, kc_lp,
+                                 vc_lp, qr, kr, rope, stream);
 }
 
 }  // namespace isa

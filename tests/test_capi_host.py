@@ -146,6 +146,33 @@ def test_backward_with_block_mask_unsupported():
     assert st == isa.ISA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("base", [-1.0, float("nan"), float("inf")])
+def test_rope_base_validation(base):
+    with pytest.raises(isa.IsaError) as e:
+        isa.isa_plan_create(1, 2, 256, 256, 128, 64, 0.5, 0.5, rope_base=base)
+    assert e.value.status == isa.ISA_ERR_INVALID_ARG
+
+
+def test_rope_workspace_holds_the_rotated_q_and_k():
+    plain = isa.isa_plan_create(2, 3, 700, 500, 128, 64, 0.5, 0.5)
+    rope = isa.isa_plan_create(2, 3, 700, 500, 128, 64, 0.5, 0.5, rope_base=10000.0)
+    tokens = 2 * 3 * 1200 * 128 * 2
+    assert rope.info["workspace_bytes"] >= plain.info["workspace_bytes"] + 2 * tokens
+    assert {k: v for k, v in rope.info.items() if k != "workspace_bytes"} == \
+        {k: v for k, v in plain.info.items() if k != "workspace_bytes"}
+
+
+def test_backward_with_rope_unsupported():
+    lib = isa._lib()
+    p = isa.isa_plan_create(1, 2, 256, 256, 128, 64, 0.5, 0.5, rope_base=10000.0)
+    fake = ctypes.c_void_p(0x1000)
+    a = isa.isa_aux_t()
+    a.sel = a.flat = a.sharp = 0x1000
+    st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
+                          fake, fake, fake, fake, 1 << 40, None)
+    assert st == isa.ISA_ERR_UNSUPPORTED
+
+
 def test_null_arguments_rejected_before_any_launch():
     lib = isa._lib()
     assert lib.isa_plan_create(None, None) == isa.ISA_ERR_INVALID_ARG
