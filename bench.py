@@ -13,8 +13,9 @@ stages on the launch stream, inside the timed region), the roofline of the
 dominant kernel (the exact path), the library's own dense attention on the same
 input, and the fp64 CPU oracle timed on a bounded sample.  Extra sections time
 the same workload with the block mask inside flat query blocks (alpha_ns,
-default 0.0625) and with the decoupled rotary embedding (base 10000), and the
-decision-frozen backward of the B=2 N=16384 workload.
+default 0.0625), with the decoupled rotary embedding (base 10000) and with
+block lengths 32 and 128, and the decision-frozen backward of the B=2 N=16384
+workload.
 """
 
 import argparse
@@ -64,6 +65,8 @@ def parse():
     ap.add_argument("--rope-base", type=float, default=10000.0,
                     help="also time the forward with the decoupled rotary embedding (0 = skip)")
     ap.add_argument("--rope-steps", type=int, default=10)
+    ap.add_argument("--block-lengths", type=int, nargs="*", default=[32, 128],
+                    help="also time the forward with these block lengths (none: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the workload line: ISA vs dense over N = 5K..64K")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -258,6 +261,26 @@ def bench_rope(args, isa, torch, q, k, v, c):
                           "hbm_frac": pool_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
 
 
+def bench_block_lengths(args, isa, torch, q, k, v, c):
+    """The same workload and input cut into blocks of other lengths (b = 32
+    and 128 beside the workload's 64): latency, the exact path's time and rate
+    (its algorithmic flops depend on b through k and the routing)."""
+    out = {}
+    for b in args.block_lengths:
+        cb = dict(c, block=b)
+        ms, stage_ms, info = _time_variant(isa, torch, q, k, v, cb, args.mask_steps)
+        N, D = c["L_src"] + c["L_ctx"], c["D"]
+        sharp_rows = min(info["n_sharp"] * b, N)  # every sharp block is whole here
+        ex_flops = 4.0 * c["B"] * c["H"] * sharp_rows * info["l_new"] * D
+        ex_ms = stage_ms["attn_exact"]
+        _log(f"block length {b}: ISA forward {ms:.3f} ms; exact path {ex_ms:.3f} ms")
+        out[str(b)] = {"latency_ms": ms, "k": info["k"], "l_new": info["l_new"],
+                       "n_flat": info["n_flat"], "stages_ms": stage_ms,
+                       "attn_exact": {"ms": ex_ms, "algorithmic_tflop": ex_flops / 1e12,
+                                      "TFLOP/s": ex_flops / (ex_ms * 1e-3) / 1e12}}
+    return out
+
+
 def bench_block_mask(args, isa, torch, q, k, v, c):
     """The same workload with the block mask inside flat query blocks
     (alpha_ns > 0): latency, stage times and the flat-path kernel's rate."""
@@ -441,6 +464,9 @@ def main():
     rope = None
     if args.rope_base > 0:
         rope = bench_rope(args, isa, torch, q, k, v, c)
+    block_lengths = None
+    if args.block_lengths:
+        block_lengths = bench_block_lengths(args, isa, torch, q, k, v, c)
 
     dense = None
     if not args.no_dense:
@@ -505,6 +531,7 @@ def main():
         "roofline": roofline,
         "block_mask": block_mask,
         "rope": rope,
+        "block_lengths": block_lengths,
         "backward": backward,
         "cpu_baseline": cpu,
     }

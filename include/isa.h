@@ -25,12 +25,13 @@
  *     device-to-host copy happens inside an entry point.
  *   - Argument errors are detected on the host before the first launch, so
  *     on error nothing has been written.  No entry point aborts or throws.
- *   - Supported on the device: block = 64, D in {64, 128}, any L_src >= 1 and
- *     L_ctx >= 0 (the source and the context are each cut into 64-token
- *     blocks from their own start, so the last block of each may be partial:
- *     [notes] key design 1 counts ceil(L_ctx / b) context blocks), dtype BF16
- *     (fp32 accumulation) or FP32.  Other valid descriptions return
- *     ISA_ERR_UNSUPPORTED.
+ *   - Supported on the device: block in {32, 64, 128}, D in {64, 128}, any
+ *     L_src >= 1 and L_ctx >= 0 (the source and the context are each cut into
+ *     b-token blocks from their own start, so the last block of each may be
+ *     partial: [notes] key design 1 counts ceil(L_ctx / b) context blocks),
+ *     dtype BF16 (fp32 accumulation) or FP32.  The block mask (n_ns > 0 with
+ *     flat blocks) needs block = 64; the backward needs block = 64.  Other
+ *     valid descriptions return ISA_ERR_UNSUPPORTED.
  */
 #ifndef ISA_H
 #define ISA_H
@@ -110,7 +111,8 @@ typedef struct {
  * Errors: ISA_ERR_INVALID_ARG (null out/desc, B/H/D/block < 1 or negative,
  * L_src < 1, L_ctx < 0, a ratio outside [0, 1] or NaN, rope_base negative,
  * infinite or NaN),
- * ISA_ERR_UNSUPPORTED (block != 64, D not 64/128, unknown dtype). */
+ * ISA_ERR_UNSUPPORTED (block not 32/64/128, D not 64/128, the block mask with
+ * flat blocks at block != 64, more than 4096 blocks per head). */
 isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc);
 
 /* Copy the derived sizes into *info.  Host only. */
@@ -167,8 +169,8 @@ isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K,
  * order given].  sel: device [B, H, k] int32 (as written by isa_forward).
  * isa_forward itself never materialises K_new: its attention kernels read
  * the same rows through the block table.  Errors: ISA_ERR_INVALID_ARG,
- * ISA_ERR_UNSUPPORTED (L_src or L_ctx not a multiple of 64: the length of
- * K_new would depend on sel), ISA_ERR_HIP. */
+ * ISA_ERR_UNSUPPORTED (L_src or L_ctx not a multiple of the block length: the
+ * length of K_new would depend on sel), ISA_ERR_HIP. */
 isa_status_t isa_gather(isa_plan_t plan, const void* K, const void* V, const int32_t* sel,
                         void* K_new, void* V_new, void* stream);
 
@@ -189,9 +191,9 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * selected receive zero.  Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D]; lse:
  * [B, H, N] float from the forward; aux: sel, flat and sharp from the
  * forward (required).  workspace: at least isa_backward_workspace_bytes().
- * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, a plan with
- * n_ns > 0 or rope_base > 0, or L_src / L_ctx not a multiple of 64),
- * ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
+ * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, block != 64, a
+ * plan with n_ns > 0 or rope_base > 0, or L_src / L_ctx not a multiple of
+ * 64), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

@@ -25,6 +25,7 @@ struct isa_plan_s {
   int64_t N;
   int32_t BH;
   BlockGrid grid;   // token layout of the blocks
+  int32_t half_shift;  // log2(block / 32): the attention kernels' 32-row slices per block
   bool aligned;     // L_src and L_ctx are multiples of the block length
   bool rope;        // decoupled rotary embedding of Q and K
   RopeFreq freq;    // its pair frequencies base^(-2i/D)
@@ -99,7 +100,8 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   if (!(d.rope_base >= 0.0) || isinf(d.rope_base)) return ISA_ERR_INVALID_ARG;
   if (d.dtype != ISA_DTYPE_BF16 && d.dtype != ISA_DTYPE_FP32) return ISA_ERR_INVALID_ARG;
   if ((int64_t)d.L_src + d.L_ctx > INT32_MAX / 2) return ISA_ERR_UNSUPPORTED;
-  if (d.block != kBlock || (d.D != 64 && d.D != 128)) return ISA_ERR_UNSUPPORTED;
+  if ((d.block != 32 && d.block != 64 && d.block != 128) || (d.D != 64 && d.D != 128))
+    return ISA_ERR_UNSUPPORTED;
   const int64_t BH = (int64_t)d.B * d.H;
   if (BH > 65535) return ISA_ERR_UNSUPPORTED;
 
@@ -109,7 +111,8 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   p->d = d;
   p->BH = (int32_t)BH;
   p->N = (int64_t)d.L_src + d.L_ctx;
-  p->aligned = d.L_src % kBlock == 0 && d.L_ctx % kBlock == 0;
+  p->aligned = d.L_src % d.block == 0 && d.L_ctx % d.block == 0;
+  p->half_shift = d.block == 32 ? 0 : (d.block == 64 ? 1 : 2);
   p->rope = d.rope_base > 0.0;
   // pair i of D/2 turns by pos * base^(-2i/D) (the exponent as -2 i / D in double)
   for (int i = 0; p->rope && i < d.D / 2; ++i)
@@ -128,9 +131,15 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   in.n_flat = flat_count(d.alpha_f, in.n_q_blocks);
   in.n_sharp = in.n_q_blocks - in.n_flat;
   in.n_ns = ns_count(d.alpha_ns, in.n_kv_blocks);
+  // the block-mask kernel is built for 64-token blocks
+  if (in.n_ns > 0 && in.n_flat > 0 && d.block != kBlock) {
+    delete p;
+    return ISA_ERR_UNSUPPORTED;
+  }
   p->grid.L_src = d.L_src;
   p->grid.n_src = (int32_t)in.n_src_blocks;
   p->grid.N = (int32_t)p->N;
+  p->grid.len = d.block;
 
   WorkspaceLayout& w = p->ws;
   size_t off = 0;
@@ -261,13 +270,17 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   pe.v = V;
   pe.o = O;
   pe.lse = lse;
+  // (both lists are read in 32-row slices, 2^half_shift per block)
+  const int hs = plan->half_shift;
   pe.q_tab = sharp;
   pe.q_tab_stride = in.n_sharp;
-  pe.n_q_entries = (int)in.n_sharp;
+  pe.n_q_slices = (int)in.n_sharp << hs;
+  pe.n_q_entries = (pe.n_q_slices + 1) / 2;
   pe.kv_tab = kv_tab;
   pe.kv_tab_stride = in.n_kv_blocks;
-  pe.kv_rows = (int)in.n_kv_blocks * kBlock;  // one 64-row tile per K_new block
-  pe.kv_row_shift = 6;
+  pe.kv_rows = 32 * ((int)in.n_kv_blocks << hs);
+  pe.kv_row_table = 0;
+  pe.half_shift = hs;
   pe.q_head_stride = plan->N * D;
   pe.kv_head_stride = plan->N * D;
   pe.lse_head_stride = plan->N;
@@ -317,9 +330,10 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   pt.v = vc_lp;
   pt.q_tab = flat;
   pt.q_tab_stride = in.n_flat;
-  pt.n_q_entries = (int)in.n_flat;
+  pt.n_q_slices = (int)in.n_flat << hs;
+  pt.n_q_entries = (pt.n_q_slices + 1) / 2;
   pt.kv_rows = (int)in.n_kv_blocks;
-  pt.kv_row_shift = 0;
+  pt.kv_row_table = 1;
   pt.kv_head_stride = (int64_t)n_q * D;
   pt.lse_offset = (float)log((double)d.block);
   ISA_LAUNCH(launch_attention(pt, d.dtype, s));
@@ -378,17 +392,20 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
   p.o = O;
   p.lse = lse;
   p.n_q_entries = N / kBlock;
+  p.n_q_slices = N / 32;
   p.kv_rows = N;
-  p.kv_row_shift = 0;
+  p.kv_row_table = 0;
+  p.half_shift = 1;
   p.q_head_stride = (int64_t)N * D;
   p.kv_head_stride = (int64_t)N * D;
   p.lse_head_stride = N;
   p.BH = B * H;
   p.D = D;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-  p.grid.L_src = N;  // no context: a plain grid of whole blocks
+  p.grid.L_src = N;  // no context: a plain grid of whole 64-token blocks
   p.grid.n_src = N / kBlock;
   p.grid.N = N;
+  p.grid.len = kBlock;
   ISA_LAUNCH(launch_attention(p, dtype, static_cast<hipStream_t>(stream)));
   return ISA_OK;
 }
@@ -445,7 +462,7 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
     if (!aligned16(q)) return ISA_ERR_INVALID_ARG;
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
   if (plan->info.n_ns > 0 && plan->info.n_flat > 0) return ISA_ERR_UNSUPPORTED;
-  if (!plan->aligned) return ISA_ERR_UNSUPPORTED;
+  if (!plan->aligned || plan->d.block != kBlock) return ISA_ERR_UNSUPPORTED;
   if (plan->rope) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;

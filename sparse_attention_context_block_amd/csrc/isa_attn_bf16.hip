@@ -73,14 +73,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const int hi = lane >> 5;
 
   // ---- this wave's 32 query rows ----
+  // (slice 2e + (wave & 1) of the query list; rows past a partial block's end
+  // read the slice's first row and are not stored)
   const int e = qt * 2 + (wave >> 1);
   const bool wave_valid = e < p.n_q_entries;
-  const int qblk = wave_valid ? (p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e) : 0;
-  // row qr of the query block; the tail rows of a partial block (last block of
-  // a segment) read its first row and are not stored
-  const int qr = (wave & 1) * 32 + l32;
-  const bool q_ok = qr < p.grid.rows(qblk);
-  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
+  const int32_t* qlist = p.q_tab ? p.q_tab + bh * p.q_tab_stride : nullptr;
+  const Slice qs = list_slice(p.grid, qlist, wave_valid ? p.n_q_slices : 0, p.half_shift,
+                              2 * e + (wave & 1));
+  const bool q_ok = l32 < qs.cnt;
+  const int64_t qrow = (int64_t)qs.start + (q_ok ? l32 : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
@@ -91,37 +92,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const bf16_bits* Kh = static_cast<const bf16_bits*>(p.k) + bh * p.kv_head_stride;
   const bf16_bits* Vh = static_cast<const bf16_bits*>(p.v) + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
-  // A 64-row tile is one contiguous 64-row block of the K/V arrays unless the
-  // table names single rows (the Taylor path): then every row is looked up.
-  const bool row_table = kRowTable;  // launcher: kv_tab set and kv_row_shift == 0
+  // Block table: tile t is the slices 2t and 2t + 1 of the block list (keys
+  // past a slice's valid rows are masked).  Row table (the Taylor path): every
+  // key row is looked up.
+  const bool row_table = kRowTable;  // launcher: kv_row_table set
+  const int kv_slices = p.kv_rows / 32;
   const int n_tiles = (p.kv_rows + kBN - 1) / kBN;
-  // block-table entry of the tile to load next, prefetched one tile ahead so
-  // its scalar load latency hides behind a whole tile of compute
-  int next_blk = (tab && !row_table) ? tab[0] : 0;
-  int tile_last = kBN - 1;  // last valid row of the block being loaded
-  auto tile_row0 = [&](int t) -> int64_t {
-    const int blk = tab ? next_blk : t;
-    if (row_table) return 0;
-    tile_last = p.grid.rows(blk) - 1;
-    const int64_t r0 = p.grid.start(blk);
-    if (tab) next_blk = (t + 1 < n_tiles) ? tab[t + 1] : 0;
-    return r0;
+  auto slice_of = [&](int eta) -> Slice {
+    return list_slice(p.grid, tab, kv_slices, p.half_shift, eta);
   };
-  auto src_row = [&](int64_t row0, int t, int r) -> int64_t {
-    if (!row_table) return row0 + min(r, tile_last);  // a partial block repeats its last row
+  Slice sl_a{0, 0}, sl_b{0, 0};  // slices of the tile being loaded (block table)
+  auto src_row = [&](int t, int r) -> int64_t {
+    if (!row_table) {  // rows past a slice's valid rows repeat its last one
+      const Slice& sl = (r & 32) ? sl_b : sl_a;
+      return (int64_t)sl.start + min(r & 31, max(sl.cnt - 1, 0));
+    }
     return tab[min(t * kBN + r, p.kv_rows - 1)];  // rows past the end: valid, then masked
   };
-  // Partial blocks (the tail of each segment).  Block-table tiles: the source
-  // tail sits at K_new position n_src - 1, the context tail (if kept) last;
-  // their missing keys are masked.  Row table (pooled rows): the same two
-  // positions carry the weight (tokens / kBlock) as a logit offset.
+  // Row table (pooled rows): the partial blocks' rows (the source tail at K_new
+  // position n_src - 1, the context tail last if kept) carry the weight
+  // (tokens / len) as a logit offset.
   const int src_tail = p.grid.src_tail();
   const int ctx_tail = p.grid.ctx_tail();
-  const int n_pos = row_table ? p.kv_rows : n_tiles;
-  const int pt0 = (tab && src_tail) ? p.grid.n_src - 1 : -1;
-  const int pt1 = (tab && ctx_tail && tab[n_pos - 1] == p.grid.n_blocks() - 1) ? n_pos - 1 : -1;
-  const float w0 = src_tail ? log2f((float)src_tail / kBN) / p.scale_log2 : 0.0f;
-  const float w1 = ctx_tail ? log2f((float)ctx_tail / kBN) / p.scale_log2 : 0.0f;
+  const int pt0 = (row_table && src_tail) ? p.grid.n_src - 1 : -1;
+  const int pt1 = (row_table && ctx_tail && tab[p.kv_rows - 1] == p.grid.n_blocks() - 1)
+                      ? p.kv_rows - 1 : -1;
+  const float w0 = src_tail ? log2f((float)src_tail / p.grid.len) / p.scale_log2 : 0.0f;
+  const float w1 = ctx_tail ? log2f((float)ctx_tail / p.grid.len) / p.scale_log2 : 0.0f;
 
   // staging registers for the next tile (named, so they stay in VGPRs)
   uint4 k0, k1, k2, k3;  // K chunks c = tid + 256 i (i < KCH <= 4)
@@ -140,11 +137,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const int vpos = (vg >> 2) * 16 + (((vq & 1) << 1) | (vq >> 1)) * 4;
 
   auto load_tile = [&](int t) {
-    const int64_t row0 = tile_row0(t);
+    if (!row_table) {
+      sl_a = slice_of(2 * t);
+      sl_b = slice_of(2 * t + 1);
+    }
 #define ISA_K_LOAD(I, R)                                                                \
   {                                                                                     \
     const int c = tid + kThreads * I;                                                   \
-    R = *reinterpret_cast<const uint4*>(Kh + src_row(row0, t, c / KC) * D + (c % KC) * 8); \
+    R = *reinterpret_cast<const uint4*>(Kh + src_row(t, c / KC) * D + (c % KC) * 8);    \
   }
     ISA_K_LOAD(0, k0)
     ISA_K_LOAD(1, k1)
@@ -155,10 +155,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
 #undef ISA_K_LOAD
     if (v_active) {
       const bf16_bits* vb = Vh + vd * 8;
-      v0 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 0) * D);
-      v1 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 1) * D);
-      v2 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 2) * D);
-      v3 = *reinterpret_cast<const uint4*>(vb + src_row(row0, t, 4 * vg + 3) * D);
+      v0 = *reinterpret_cast<const uint4*>(vb + src_row(t, 4 * vg + 0) * D);
+      v1 = *reinterpret_cast<const uint4*>(vb + src_row(t, 4 * vg + 1) * D);
+      v2 = *reinterpret_cast<const uint4*>(vb + src_row(t, 4 * vg + 2) * D);
+      v3 = *reinterpret_cast<const uint4*>(vb + src_row(t, 4 * vg + 3) * D);
     }
   };
   auto store_tile = [&](int buf) {
@@ -251,14 +251,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
           }
       }
     } else {
-      const int vt = (t == pt0) ? src_tail : ((t == pt1) ? ctx_tail : kBN);
-      if (vt < kBN) {
+      const Slice ta = slice_of(2 * t), tb = slice_of(2 * t + 1);
+      if (ta.cnt < 32 || tb.cnt < 32) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= vt) sacc[s][r] = -INFINITY;
+            const int key = 8 * (r >> 2) + 4 * hi + (r & 3);  // within slice s
+            if (key >= (s ? tb.cnt : ta.cnt)) sacc[s][r] = -INFINITY;
           }
       }
     }
@@ -357,7 +357,8 @@ hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
   const int wg_per_head = (p.n_q_entries + 1) / 2;
   const int64_t total = (int64_t)wg_per_head * p.BH;
   const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-  const bool row_table = p.kv_tab && p.kv_row_shift == 0;
+  const bool row_table = p.kv_row_table != 0;
+  if (!row_table && p.kv_rows % 32 != 0) return hipErrorInvalidValue;
   if (p.D == 128) {
     if (row_table)
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, dim3(kThreads), 0, stream, p);

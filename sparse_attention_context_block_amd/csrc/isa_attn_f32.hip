@@ -24,25 +24,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const int row = tid >> 2, part = tid & 3;
-  const int qblk = p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e;
-  // the tail rows of a partial query block read its first row and are not stored
-  const bool q_ok = row < p.grid.rows(qblk);
-  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? row : 0);
+  // query row: row 31 & row of slice 2e + row / 32 of the query list; rows past
+  // a partial block's end read the slice's first row and are not stored
+  const int32_t* qlist = p.q_tab ? p.q_tab + bh * p.q_tab_stride : nullptr;
+  const Slice qs = list_slice(p.grid, qlist, p.n_q_slices, p.half_shift, 2 * e + (row >> 5));
+  const bool q_ok = (row & 31) < qs.cnt;
+  const int64_t qrow = (int64_t)qs.start + (q_ok ? (row & 31) : 0);
   const float* Qh = static_cast<const float*>(p.q) + bh * p.q_head_stride;
   const float* Kh = static_cast<const float*>(p.k) + bh * p.kv_head_stride;
   const float* Vh = static_cast<const float*>(p.v) + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
-  const int shift = p.kv_row_shift;
-  const int rmask = (1 << shift) - 1;
-  // Partial blocks (the tail of each segment) sit at K_new positions n_src - 1
-  // and, if the context tail is kept, last.  Block table: their missing tokens
-  // are skipped; row table (pooled rows): they carry the weight (tokens / b).
+  // Block table: virtual key row r is row r & 31 of slice r / 32 of the block
+  // list; rows past a slice's valid rows are skipped.  Row table (pooled rows):
+  // the partial blocks' rows (the source tail at K_new position n_src - 1, the
+  // context tail last if kept) carry the weight (tokens / len).
+  const bool row_table = p.kv_row_table != 0;
+  const int kv_slices = p.kv_rows / 32;
   const int src_tail = p.grid.src_tail(), ctx_tail = p.grid.ctx_tail();
-  const int n_pos = shift ? (p.kv_rows >> shift) : p.kv_rows;
-  const int pu0 = (tab && src_tail) ? p.grid.n_src - 1 : -1;
-  const int pu1 = (tab && ctx_tail && tab[n_pos - 1] == p.grid.n_blocks() - 1) ? n_pos - 1 : -1;
-  const float lw0 = src_tail ? logf((float)src_tail / kBlock) : 0.0f;
-  const float lw1 = ctx_tail ? logf((float)ctx_tail / kBlock) : 0.0f;
+  const int pu0 = (row_table && src_tail) ? p.grid.n_src - 1 : -1;
+  const int pu1 = (row_table && ctx_tail && tab[p.kv_rows - 1] == p.grid.n_blocks() - 1)
+                      ? p.kv_rows - 1 : -1;
+  const float lw0 = src_tail ? logf((float)src_tail / p.grid.len) : 0.0f;
+  const float lw1 = ctx_tail ? logf((float)ctx_tail / p.grid.len) : 0.0f;
 
   float q[DP], o[DP];
 #pragma unroll
@@ -58,13 +61,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
     __syncthreads();
     for (int i = tid; i < kTile * (D / 4); i += kThreads) {
       const int r = i / (D / 4), c = (i % (D / 4)) * 4;
-      int rr = min(t0 + r, p.kv_rows - 1);
-      int64_t src = rr;
-      if (tab && shift) {
-        const int blk = tab[rr >> shift];
-        src = (int64_t)p.grid.start(blk) + min(rr & rmask, p.grid.rows(blk) - 1);
-      } else if (tab) {
-        src = tab[rr];
+      const int rr = min(t0 + r, p.kv_rows - 1);
+      int64_t src;
+      if (!row_table) {
+        const Slice sl = list_slice(p.grid, tab, kv_slices, p.half_shift, rr >> 5);
+        src = (int64_t)sl.start + min(rr & 31, max(sl.cnt - 1, 0));
+      } else {
+        src = tab ? tab[rr] : rr;
       }
       *reinterpret_cast<float4*>(&Ks[r][c]) = *reinterpret_cast<const float4*>(Kh + src * D + c);
       *reinterpret_cast<float4*>(&Vs[r][c]) = *reinterpret_cast<const float4*>(Vh + src * D + c);
@@ -73,11 +76,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
     for (int j = 0; j < n; ++j) {
       const int rr = t0 + j;
       float wbias = 0.0f;
-      if (tab && shift) {
-        const int pos = rr >> shift;
-        const int vt = (pos == pu0) ? src_tail : ((pos == pu1) ? ctx_tail : kBlock);
-        if ((rr & rmask) >= vt) continue;  // past a partial block's tail
-      } else if (tab) {
+      if (!row_table) {
+        if ((rr & 31) >= list_slice(p.grid, tab, kv_slices, p.half_shift, rr >> 5).cnt)
+          continue;  // past a partial block's end, or an empty slice
+      } else {
         wbias = (rr == pu0) ? lw0 : ((rr == pu1) ? lw1 : 0.0f);
       }
       float s = 0.0f;
@@ -116,9 +118,8 @@ bool force_4wave() {
 
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream) {
   if (dtype == ISA_DTYPE_BF16) {
-    // whole 64-row key tiles (block table or contiguous keys): ping-pong kernel
-    const bool row_table = p.kv_tab && p.kv_row_shift == 0;
-    if (!row_table && p.kv_rows >= 64 && p.kv_rows % 64 == 0 && !force_4wave()) return launch_attention_pp(p, stream);
+    // block tables (exact path, dense): the ping-pong kernel
+    if (!p.kv_row_table && !force_4wave()) return launch_attention_pp(p, stream);
     return launch_attention_bf16(p, stream);
   }
   if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;

@@ -46,7 +46,7 @@ struct Lds {
   static constexpr int kTotal = 2 * kKBytes + 2 * kVBytes;
 };
 
-template <int D>
+template <int D, int kShift>  // kShift: log2 of the 32-row slices per block
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) {
   using S = Lds<D>;
   constexpr int KC = D / 8;                  // 16-byte chunks per row
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   const int per_xcd = (total + 7) / 8;
   const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   // whole workgroup, before any barrier (the barrier counts below assume >= 1 tile)
-  if (lid >= total || p.kv_rows < kBN) return;
+  if (lid >= total || p.kv_rows < 32) return;
   const int64_t bh = lid / wg_per_head;
   const int qt = lid % wg_per_head;
 
@@ -75,33 +75,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   const int hi = lane >> 5;
 
   // ---- this wave's 32 query rows ----
+  // (slice 2e + (wave & 1) of the query list; rows past a partial block's end
+  // read the slice's first row and are not stored)
   const int e = qt * 4 + (wave >> 1);
   const bool wave_valid = e < p.n_q_entries;
-  const int qblk = wave_valid ? (p.q_tab ? p.q_tab[bh * p.q_tab_stride + e] : e) : 0;
-  // row qr of the query block; the tail rows of a partial block (last block of
-  // a segment) read its first row and are not stored
-  const int qr = (wave & 1) * 32 + l32;
-  const bool q_ok = qr < p.grid.rows(qblk);
-  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
+  const int32_t* qlist = p.q_tab ? p.q_tab + bh * p.q_tab_stride : nullptr;
+  const Slice qs = list_slice(p.grid, qlist, wave_valid ? p.n_q_slices : 0, kShift,
+                              2 * e + (wave & 1));
+  const bool q_ok = l32 < qs.cnt;
+  const int64_t qrow = (int64_t)qs.start + (q_ok ? l32 : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     qreg[kk] = *reinterpret_cast<const bf16x8_t*>(Qh + qrow * D + 16 * kk + 8 * hi);
 
-  // ---- key tiles: tile u is the contiguous 64-row block blk_of(u) ----
+  // ---- key tiles: tile u is the slices 2u and 2u + 1 of the block table ----
   const bf16_bits* Kh = static_cast<const bf16_bits*>(p.k) + bh * p.kv_head_stride;
   const bf16_bits* Vh = static_cast<const bf16_bits*>(p.v) + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
-  const int n_tiles = p.kv_rows / kBN;  // exact path and dense: one tile per block
-  auto blk_of = [&](int u) -> int { return tab ? tab[u] : u; };
-  // tiles holding a partial block: the source tail sits at K_new position
-  // n_src - 1, the context tail (if kept) last; their missing keys are masked
-  const int src_tail = p.grid.src_tail();
-  const int ctx_tail = p.grid.ctx_tail();
-  const int pt0 = src_tail ? p.grid.n_src - 1 : -1;
-  const int pt1 =
-      (ctx_tail && tab && tab[n_tiles - 1] == p.grid.n_blocks() - 1) ? n_tiles - 1 : -1;
+  const int kv_slices = p.kv_rows / 32;
+  const int n_tiles = (kv_slices + 1) / 2;
+  // the two slices of tile u; keys past a slice's valid rows (partial blocks,
+  // an odd slice count) are masked
+  struct TileSrc {
+    Slice a, b;
+  };
+  auto tile_src = [&](int u) -> TileSrc {
+    TileSrc ts;
+    tile_slices<kShift>(p.grid, tab, kv_slices, u, ts.a, ts.b);
+    return ts;
+  };
 
   // group A stages K: chunk c = gtid + 256 i -> row c / KC, column chunk c % KC
   uint4 k0, k1, k2, k3;
@@ -115,13 +119,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   auto k_lds = [&](int b) { return smem + b * S::kKBytes; };
   auto v_lds = [&](int b) { return smem + 2 * S::kKBytes + b * S::kVBytes; };
 
-  auto load_k = [&](int blk) __attribute__((always_inline)) {
-    const bf16_bits* base = Kh + (int64_t)p.grid.start(blk) * D;
-    const int last = p.grid.rows(blk) - 1;  // rows past a partial block repeat its last row
+  auto load_k = [&](const TileSrc& ts) __attribute__((always_inline)) {
+    // rows past a slice's valid rows repeat its last one (they are masked)
+    const bf16_bits* base_a = Kh + (int64_t)ts.a.start * D;
+    const bf16_bits* base_b = Kh + (int64_t)ts.b.start * D;
+    const int last_a = max(ts.a.cnt - 1, 0), last_b = max(ts.b.cnt - 1, 0);
+    // chunk c = gtid + 256 I is row c / KC: slice ((256 / KC) I) / 32 of the tile
 #define ISA_K_LOAD(I, R)                                                                \
   {                                                                                     \
     const int c = gtid + kGroup * I;                                                    \
-    R = *reinterpret_cast<const uint4*>(base + min(c / KC, last) * D + (c % KC) * 8);            \
+    constexpr bool kSecond = ((kGroup / KC) * I) / 32 != 0;                             \
+    const int row = min((c / KC) & 31, kSecond ? last_b : last_a);                      \
+    R = *reinterpret_cast<const uint4*>((kSecond ? base_b : base_a) + row * D + (c % KC) * 8); \
   }
     ISA_K_LOAD(0, k0)
     ISA_K_LOAD(1, k1)
@@ -146,14 +155,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
     }
 #undef ISA_K_STORE
   };
-  auto load_v = [&](int blk) __attribute__((always_inline)) {
+  auto load_v = [&](const TileSrc& ts) __attribute__((always_inline)) {
     if (v_active) {
-      const bf16_bits* vb = Vh + (int64_t)p.grid.start(blk) * D + vd * 8;
-      const int last = p.grid.rows(blk) - 1;
-      v0 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 0, last) * D);
-      v1 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 1, last) * D);
-      v2 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 2, last) * D);
-      v3 = *reinterpret_cast<const uint4*>(vb + min(4 * vg + 3, last) * D);
+      // keys 4 vg .. 4 vg + 3 lie in slice vg / 8 of the tile
+      const bool second = vg >= 8;
+      const bf16_bits* vb = Vh + (int64_t)(second ? ts.b.start : ts.a.start) * D + vd * 8;
+      const int last = max((second ? ts.b.cnt : ts.a.cnt) - 1, 0);
+      const int r0 = 4 * (vg & 7);
+      v0 = *reinterpret_cast<const uint4*>(vb + min(r0 + 0, last) * D);
+      v1 = *reinterpret_cast<const uint4*>(vb + min(r0 + 1, last) * D);
+      v2 = *reinterpret_cast<const uint4*>(vb + min(r0 + 2, last) * D);
+      v3 = *reinterpret_cast<const uint4*>(vb + min(r0 + 3, last) * D);
     }
   };
   auto store_v = [&](int b) __attribute__((always_inline)) {
@@ -201,15 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   };
   // online softmax of sacc (exp2 domain) into the packed P^T operands
   auto softmax = [&](int t) __attribute__((always_inline)) {
-    const int vt = (t == pt0) ? src_tail : ((t == pt1) ? ctx_tail : kBN);
-    if (vt < kBN) {
+    {
+      const TileSrc ts = tile_src(t);
+      if (ts.a.cnt < 32 || ts.b.cnt < 32) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= vt) sacc[s][r] = -INFINITY;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int key = 8 * (r >> 2) + 4 * hi + (r & 3);  // within slice s
+            if (key >= (s ? ts.b.cnt : ts.a.cnt)) sacc[s][r] = -INFINITY;
+          }
+      }
     }
     float tmax = sacc[0][0];
 #pragma unroll
@@ -264,12 +278,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   };
 
   // ---- prologue (phase -1 and phase 0; B also phase 1) ----
-  int e_next = blk_of(min(1, n_tiles - 1));  // entry of the next tile this group loads
+  TileSrc e_next = tile_src(min(1, n_tiles - 1));  // the next tile this group loads
   if (gA) {
-    load_k(blk_of(0));
+    load_k(tile_src(0));
     store_k(0);
   } else {
-    load_v(blk_of(0));
+    load_v(tile_src(0));
   }
   phase_barrier();                                 // barrier 1
   if (gA) {                                        // phase 0: A computes S(0)
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
     store_v(0);
     if (n_tiles > 1) load_v(e_next);
   }
-  e_next = blk_of(min(2, n_tiles - 1));
+  e_next = tile_src(min(2, n_tiles - 1));
   phase_barrier();                                 // barrier 2
   if (!gA) {                                       // phase 1: B computes S(0)
     qk(k_lds(0));
@@ -290,8 +304,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   for (int t = 0; t < n_tiles; ++t) {
     softmax(t);
     if (t + 1 < n_tiles) {
-      const int ent = e_next;
-      e_next = blk_of(min(t + 3, n_tiles - 1));
+      const TileSrc ent = e_next;
+      e_next = tile_src(min(t + 3, n_tiles - 1));
       if (gA) {
         store_k((t + 1) & 1);
         if (t + 2 < n_tiles) load_k(ent);
@@ -345,14 +359,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
 
 hipError_t launch_attention_pp(const AttnParams& p, hipStream_t stream) {
   if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;
-  if (p.kv_rows < kBN || p.kv_rows % kBN != 0) return hipErrorInvalidValue;
+  if (p.kv_rows < 32 || p.kv_rows % 32 != 0 || p.kv_row_table) return hipErrorInvalidValue;
+  if (p.half_shift < 0 || p.half_shift > 2) return hipErrorInvalidValue;
   const int wg_per_head = (p.n_q_entries + 3) / 4;
   const int64_t total = (int64_t)wg_per_head * p.BH;
   const dim3 grid((unsigned)(((total + 7) / 8) * 8));
-  if (p.D == 128)
-    hipLaunchKernelGGL(attn_fwd_pp_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_fwd_pp_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+#define ISA_PP_LAUNCH(DD, SH) \
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<DD, SH>), grid, dim3(kThreads), 0, stream, p)
+  if (p.D == 128) {
+    if (p.half_shift == 1) ISA_PP_LAUNCH(128, 1);
+    else if (p.half_shift == 0) ISA_PP_LAUNCH(128, 0);
+    else ISA_PP_LAUNCH(128, 2);
+  } else {
+    if (p.half_shift == 1) ISA_PP_LAUNCH(64, 1);
+    else if (p.half_shift == 0) ISA_PP_LAUNCH(64, 0);
+    else ISA_PP_LAUNCH(64, 2);
+  }
+#undef ISA_PP_LAUNCH
   return hipGetLastError();
 }
 

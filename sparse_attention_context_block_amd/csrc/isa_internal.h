@@ -31,43 +31,93 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(double x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Block length the device kernels are built for (tokens per pooled block;
-// also the key-tile height of the attention kernels).
+// Height of the attention kernels' key and query tiles, and the block length
+// of the kernels that are built for one (the block-mask kernel, the backward).
 constexpr int kBlock = 64;
 
 // Block grid of a [source | context] sequence ([notes] key design 1 counts
 // ceil(L_ctx / b) context blocks): the source and the context are each cut
-// into kBlock-token blocks from their own start, so the last block of each
-// segment may be partial.  Block b starts at kBlock * b (b < n_src) or at
-// L_src + kBlock * (b - n_src) and holds min(kBlock, segment end - start)
-// tokens.  A sequence without context (L_src = N) is a plain grid.
+// into len-token blocks from their own start, so the last block of each
+// segment may be partial.  Block b starts at len * b (b < n_src) or at
+// L_src + len * (b - n_src) and holds min(len, segment end - start) tokens.
+// A sequence without context (L_src = N) is a plain grid.
 struct BlockGrid {
   int32_t L_src;  // tokens of the source segment
-  int32_t n_src;  // its blocks, ceil(L_src / kBlock)
+  int32_t n_src;  // its blocks, ceil(L_src / len)
   int32_t N;      // all tokens
+  int32_t len;    // block length b
   __host__ __device__ __forceinline__ int start(int b) const {
-    return b < n_src ? b * kBlock : L_src + (b - n_src) * kBlock;
+    return b < n_src ? b * len : L_src + (b - n_src) * len;
   }
   __host__ __device__ __forceinline__ int rows(int b) const {
     const int end = b < n_src ? L_src : N;
     const int n = end - start(b);
-    return n < kBlock ? n : kBlock;
+    return n < len ? n : len;
   }
   __host__ __device__ __forceinline__ int n_blocks() const {
-    return n_src + (N - L_src + kBlock - 1) / kBlock;
+    return n_src + (N - L_src + len - 1) / len;
   }
   // tokens of the partial last block of each segment (0: the segment is whole)
-  __host__ __device__ __forceinline__ int src_tail() const { return L_src % kBlock; }
-  __host__ __device__ __forceinline__ int ctx_tail() const { return (N - L_src) % kBlock; }
+  __host__ __device__ __forceinline__ int src_tail() const { return L_src % len; }
+  __host__ __device__ __forceinline__ int ctx_tail() const { return (N - L_src) % len; }
 };
+
+// A 32-row slice of a block list.  With 2^shift slices per block (len =
+// 32 << shift), slice eta of the list is rows 32 sub .. 32 sub + 31 of block
+// list[eta >> shift] (list NULL: block eta >> shift), sub = eta mod 2^shift;
+// only the rows inside the block count.  A slice past the list's n_slices, or
+// past the end of a partial block, is empty (cnt 0) and starts at a valid row
+// of the head.  The attention kernels' 64-row tiles are slices 2u and 2u + 1.
+struct Slice {
+  int32_t start;  // first token row
+  int32_t cnt;    // valid rows, 0..32
+};
+__device__ __forceinline__ Slice list_slice(const BlockGrid& g, const int32_t* list,
+                                            int n_slices, int shift, int eta) {
+  if (eta >= n_slices) return Slice{0, 0};
+  const int e = eta >> shift, sub = eta & ((1 << shift) - 1);
+  const int blk = list ? list[e] : e;
+  const int st = g.start(blk);
+  const int cnt = g.rows(blk) - 32 * sub;
+  if (cnt <= 0) return Slice{st, 0};
+  return Slice{st + 32 * sub, cnt < 32 ? cnt : 32};
+}
+
+// The two slices 2u and 2u + 1 (key tile u) of a block list with 2^kShift
+// slices per block, made wave-uniform (scalar registers) for the tile loops.
+// With kShift >= 1 both lie in one block, list[u >> (kShift - 1)].
+template <int kShift>
+__device__ __forceinline__ void tile_slices(const BlockGrid& g, const int32_t* list,
+                                            int n_slices, int u, Slice& a, Slice& b) {
+  if constexpr (kShift == 0) {
+    a = list_slice(g, list, n_slices, 0, 2 * u);
+    b = list_slice(g, list, n_slices, 0, 2 * u + 1);
+  } else {
+    const int e = u >> (kShift - 1);
+    const int sub = (u & ((1 << (kShift - 1)) - 1)) * 2;
+    const int blk = list ? list[e] : e;
+    const int st = g.start(blk), rows = g.rows(blk);
+    const int ca = min(max(rows - 32 * sub, 0), 32);
+    const int cb = min(max(rows - 32 * (sub + 1), 0), 32);
+    a = Slice{ca > 0 ? st + 32 * sub : st, ca};
+    b = Slice{cb > 0 ? st + 32 * (sub + 1) : st, cb};
+  }
+  a.start = __builtin_amdgcn_readfirstlane(a.start);
+  a.cnt = __builtin_amdgcn_readfirstlane(a.cnt);
+  b.start = __builtin_amdgcn_readfirstlane(b.start);
+  b.cnt = __builtin_amdgcn_readfirstlane(b.cnt);
+}
 
 // ---------------------------------------------------------------------------
 // Attention launch description shared by the exact path, the 0-th order
-// Taylor path and the dense baseline.  Queries come in 64-row blocks listed in
-// q_tab (NULL: block e is block e); keys/values are the rows of a virtual
-// K_new whose row r lives at source row
-//     kv_tab[r >> kv_row_shift] * 2^kv_row_shift + (r & (2^kv_row_shift - 1))
-// of the per-head K/V arrays (kv_tab NULL: row r is row r).
+// Taylor path and the dense baseline.  Blocks have grid.len = 32 << half_shift
+// tokens.  Query rows: the 32-row slices of the blocks listed in q_tab (NULL:
+// block e is block e), n_q_slices of them; 64-row query tile e is slices 2e
+// and 2e + 1.  Keys: with a block table (kv_row_table = 0) the slices of the
+// blocks listed in kv_tab (NULL: identity), kv_rows / 32 of them, key tile u
+// being slices 2u and 2u + 1 and empty rows masked; with a row table
+// (kv_row_table = 1) key r is row kv_tab[r] of the K/V arrays (pooled block
+// rows of the Taylor path), kv_rows keys.
 // ---------------------------------------------------------------------------
 struct AttnParams {
   const void* q;
@@ -77,11 +127,13 @@ struct AttnParams {
   float* lse;                // may be null
   const int32_t* q_tab;      // [BH][q_tab_stride] or null
   int64_t q_tab_stride;
-  int32_t n_q_entries;       // 64-row query blocks per head
+  int32_t n_q_entries;       // 64-row query tiles per head, ceil(n_q_slices / 2)
+  int32_t n_q_slices;        // 32-row query slices per head
   const int32_t* kv_tab;     // [BH][kv_tab_stride] or null
   int64_t kv_tab_stride;
-  int32_t kv_rows;           // rows of the virtual K_new per head (>= 1)
-  int32_t kv_row_shift;      // 6 (entries name 64-row blocks) or 0 (entries name rows)
+  int32_t kv_rows;           // keys per head: 32 per slice (block table) or one per row
+  int32_t kv_row_table;      // 1: kv_tab names rows; 0: kv_tab names blocks
+  int32_t half_shift;        // log2(grid.len / 32)
   int64_t q_head_stride;     // elements between heads of Q and O
   int64_t kv_head_stride;    // elements between heads of the K/V arrays
   int64_t lse_head_stride;   // floats between heads of lse
@@ -89,11 +141,10 @@ struct AttnParams {
   int32_t D;
   float scale_log2;          // log2(e) / sqrt(D)
   float lse_offset;          // added to every lse (ln of a uniform block weight)
-  // token layout of the query rows (and of the key rows for a block table):
-  // query block e holds grid.rows(e) rows from grid.start(e); a block-table
-  // key tile holds grid.rows(blk) keys, the rest of the tile is masked.  With
-  // a row table the keys are pooled block rows: a partial block's row enters
-  // with the extra weight log of (its tokens / kBlock).
+  // token layout of the blocks.  With a row table the keys are pooled block
+  // rows: a partial block's row (K_new position n_src - 1 for the source
+  // tail, the last position for a kept context tail) enters with the extra
+  // weight log of (its tokens / len).
   BlockGrid grid;
 };
 

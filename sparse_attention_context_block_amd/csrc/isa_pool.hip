@@ -77,7 +77,10 @@ __device__ inline void rotate_pair(double& x, double& y, double c, double s) {
 constexpr int kThreads = 256;
 constexpr int kRopeHeads = 8;  // heads per workgroup when the kernel also rotates
 
-template <typename T, int D, bool kRope>
+// kMode: 0 no rotation; 1 rotation with the angles of a block (of at most
+// kBlock rows) computed once for a group of kRopeHeads heads; 2 rotation with
+// the angles computed per row and head (longer blocks).
+template <typename T, int D, int kMode>
 __global__ __launch_bounds__(kThreads) void pool_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int BH, int N,
     int L_src, int n_src, int n_q, int block, double* __restrict__ qc, double* __restrict__ kc,
@@ -86,9 +89,11 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
   constexpr int EPC = Elt<T>::kPerChunk;
   constexpr int CH = D / EPC;          // 16-byte chunks per row
   constexpr int RP = kThreads / CH;    // rows covered per pass
-  constexpr int JMAX = (kBlock + RP - 1) / RP;  // rows per thread of a block (rotation)
-  // heads per workgroup: with the rotation, one block's angles serve this many heads
-  constexpr int kHeads = kRope ? kRopeHeads : 1;
+  constexpr bool kRope = kMode != 0;
+  constexpr bool kCache = kMode == 1;
+  constexpr int JMAX = (kBlock + RP - 1) / RP;  // rows per thread of a block (angle cache)
+  // heads per workgroup: with the angle cache, one block's angles serve this many heads
+  constexpr int kHeads = kCache ? kRopeHeads : 1;
   __shared__ double red[3][RP][D];
 
   const int blk = blockIdx.x;
@@ -110,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
 
   // rotation angles of this thread's rows (r0 + RP j) and pairs (dims
   // c EPC + 2 p, c EPC + 2 p + 1), computed once for all heads of the group
-  double cs[kRope ? JMAX : 1][EPC / 2], sn[kRope ? JMAX : 1][EPC / 2];
-  if constexpr (kRope) {
+  double cs[kCache ? JMAX : 1][EPC / 2], sn[kCache ? JMAX : 1][EPC / 2];
+  if constexpr (kCache) {
 #pragma unroll
     for (int j = 0; j < JMAX; ++j) {
       const int t = start + r0 + RP * j;
@@ -143,8 +148,17 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
       if constexpr (kRope) {
 #pragma unroll
         for (int pr = 0; pr < EPC / 2; ++pr) {
-          rotate_pair(x[2 * pr], x[2 * pr + 1], cs[j][pr], sn[j][pr]);
-          rotate_pair(y[2 * pr], y[2 * pr + 1], cs[j][pr], sn[j][pr]);
+          double c_, s_;
+          if constexpr (kCache) {
+            c_ = cs[j][pr];
+            s_ = sn[j][pr];
+          } else {
+            const int t = start + r;
+            const double pos = (double)(t < L_src ? t : t - L_src);
+            sincos(pos * rope.inv_freq[c * (EPC / 2) + pr], &s_, &c_);
+          }
+          rotate_pair(x[2 * pr], x[2 * pr + 1], c_, s_);
+          rotate_pair(y[2 * pr], y[2 * pr + 1], c_, s_);
         }
         *reinterpret_cast<uint4*>(qr + off) = Elt<T>::round_pack(x);
         *reinterpret_cast<uint4*>(kr + off) = Elt<T>::round_pack(y);
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[2][e] += x[e];
     };
-    if constexpr (kRope) {
+    if constexpr (kCache) {
       // the launcher guarantees block <= kBlock, so JMAX passes cover a block
 #pragma unroll
       for (int j = 0; j < JMAX; ++j)
@@ -196,17 +210,23 @@ hipError_t launch_typed(const void* Q, const void* K, const void* V, int BH, int
                         int L_src, int n_src, int n_q, int block, double* qc, double* kc,
                         void* kc_lp, void* vc_lp, void* qr, void* kr, const RopeFreq* rope,
                         hipStream_t stream) {
-  if (rope) {
-    if (block > kBlock) return hipErrorInvalidValue;  // the angle cache covers kBlock rows
+  if (rope && block > kBlock) {  // the angle cache covers kBlock rows
+    dim3 grid(n_q, BH);
+    hipLaunchKernelGGL((pool_kernel<T, D, 2>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(Q), static_cast<const T*>(K),
+                       static_cast<const T*>(V), BH, N, L_src, n_src, n_q, block, qc, kc,
+                       static_cast<T*>(kc_lp), static_cast<T*>(vc_lp), static_cast<T*>(qr),
+                       static_cast<T*>(kr), *rope);
+  } else if (rope) {
     dim3 grid(n_q, (BH + kRopeHeads - 1) / kRopeHeads);
-    hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((pool_kernel<T, D, 1>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(Q), static_cast<const T*>(K),
                        static_cast<const T*>(V), BH, N, L_src, n_src, n_q, block, qc, kc,
                        static_cast<T*>(kc_lp), static_cast<T*>(vc_lp), static_cast<T*>(qr),
                        static_cast<T*>(kr), *rope);
   } else {
     dim3 grid(n_q, BH);
-    hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((pool_kernel<T, D, 0>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(Q), static_cast<const T*>(K),
                        static_cast<const T*>(V), BH, N, L_src, n_src, n_q, block, qc, kc,
                        static_cast<T*>(kc_lp), static_cast<T*>(vc_lp), nullptr, nullptr,

@@ -82,7 +82,11 @@ def test_plan_counts_follow_the_rounding_rule(alpha_s, alpha_f):
     (dict(alpha_s=1.5), isa.ISA_ERR_INVALID_ARG),
     (dict(alpha_f=-0.1), isa.ISA_ERR_INVALID_ARG),
     (dict(alpha_s=float("nan")), isa.ISA_ERR_INVALID_ARG),
-    (dict(block=32), isa.ISA_ERR_UNSUPPORTED),
+    (dict(block=96), isa.ISA_ERR_UNSUPPORTED),
+    (dict(block=16), isa.ISA_ERR_UNSUPPORTED),
+    (dict(block=256), isa.ISA_ERR_UNSUPPORTED),
+    (dict(block=32, alpha_ns=0.25), isa.ISA_ERR_UNSUPPORTED),   # the block mask needs b = 64
+    (dict(block=128, alpha_ns=0.25), isa.ISA_ERR_UNSUPPORTED),
     (dict(D=96), isa.ISA_ERR_UNSUPPORTED),
     (dict(alpha_ns=1.5), isa.ISA_ERR_INVALID_ARG),
     (dict(L_src=64 * 4097, L_ctx=0), isa.ISA_ERR_UNSUPPORTED),
@@ -171,6 +175,31 @@ def test_backward_with_rope_unsupported():
     st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
                           fake, fake, fake, fake, 1 << 40, None)
     assert st == isa.ISA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("block,L_src,L_ctx", [(32, 500, 300), (128, 1000, 700), (32, 512, 384),
+                                               (128, 1024, 0)])
+def test_other_block_lengths_follow_the_oracle_counts(block, L_src, L_ctx):
+    p = isa.isa_plan_create(1, 2, L_src, L_ctx, 128, block, 0.34, 0.5)
+    starts, ends, n_src, n_ctx = orc.block_grid(L_src, L_ctx, block)
+    assert (p.info["n_src_blocks"], p.info["n_ctx_blocks"]) == (n_src, n_ctx)
+    assert p.info["k"] == orc.select_count(0.34, n_ctx)
+    assert p.info["n_flat"] == orc.flat_count(0.5, len(starts))
+    # the block mask is refused only when some query block is flat
+    q = isa.isa_plan_create(1, 2, L_src, L_ctx, 128, block, 0.34, 0.0, 0.5)
+    assert q.info["n_flat"] == 0
+
+
+def test_backward_needs_64_token_blocks():
+    lib = isa._lib()
+    fake = ctypes.c_void_p(0x1000)
+    a = isa.isa_aux_t()
+    a.sel = a.flat = a.sharp = 0x1000
+    for block in (32, 128):
+        p = isa.isa_plan_create(1, 2, 512, 512, 128, block, 0.5, 0.5)
+        st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
+                              fake, fake, fake, fake, 1 << 40, None)
+        assert st == isa.ISA_ERR_UNSUPPORTED
 
 
 def test_null_arguments_rejected_before_any_launch():
