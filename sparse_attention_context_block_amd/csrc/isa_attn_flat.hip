@@ -8,54 +8,76 @@
 // The weight b is carried as -log2(b) on the exact tokens (exp2 domain) and
 // +ln(b) on the LSE, so the representative terms need no scaling.
 //
-// One workgroup = 2 waves = one flat query block (64 rows, 32 per wave); the
-// key tiles of a block are its own, so workgroups do not share them.  Tiles:
+// One workgroup = 4 waves = one flat query block (64 rows, 16 per wave); the
+// key tiles of a block are its own, so workgroups do not share them and the
+// kernel is bound by the latency of its tile loads.  It is therefore built to
+// keep many tiles in flight: v_mfma_f32_16x16x32_bf16 on 16 query rows per
+// wave keeps a wave under 128 VGPRs, and one K and one V buffer (the next
+// tile waits in registers) keep a workgroup at 36 KB of LDS, so four
+// workgroups share a CU.  Tiles:
 //   t < n_ns:   the 64 tokens of K_new block ns[t] (rows of K, V);
 //   t >= n_ns:  64 representative rows u = 64 (t - n_ns) + r of K_new
 //               (rows of the pooled K^c, V^c), masked past n_kv and for the
 //               blocks already taken exactly (an LDS bitmap).
-// The MFMA layout, the transposed V staging and the lazy rescale are those of
-// the other bf16 attention kernels (S^T = K Q^T, O^T += V^T P^T with
-// v_mfma_f32_32x32x16_bf16, one query per lane column).
+// Layout (lane l, q = l % 16, g = l / 16): S^T = K Q^T in 16x16 subtiles, lane
+// holding keys 16 st + 4 g + i of query q; P^T enters O^T += V^T P^T as the B
+// operand with 32-key chunks whose eight slots of group g are keys
+// 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3) -- exactly the registers
+// the S^T accumulators leave in the lane, so P needs no shuffle.  V stays
+// row-major in LDS (a plain copy) and the matching V^T operand comes from two
+// transposing reads (ds_read_b64_tr_b16) per chunk.
 #include "isa_internal.h"
 
 namespace isa {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;
 constexpr int kBN = 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D>
 struct FlatSmem {
+  // K rows: 16 lanes read one 16-byte chunk of 16 consecutive rows (stride
+  // 16 mod 256 bytes: all banks).  V rows: a transposing read touches 8 bytes
+  // of 16 rows, 4 per key row (stride 32 mod 256: every 8 rows cover the banks)
   static constexpr int kKStride = D * 2 + 16;
-  static constexpr int kVStride = kBN * 2 + 16;
+  static constexpr int kVStride = D * 2 + 32;
   static constexpr int kKBytes = kBN * kKStride;
-  static constexpr int kVBytes = D * kVStride;
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kMaskOff = 2 * kStage;
+  static constexpr int kVBytes = kBN * kVStride;
+  static constexpr int kMaskOff = kKBytes + kVBytes;
   static constexpr int kTotal = kMaskOff + kMaxBlocksPerHead / 8;
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams p) {
+__global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams p) {
   using S = FlatSmem<D>;
   constexpr int KC = D / 8;                 // 16-byte chunks per row
-  constexpr int KCH = kBN * KC / kThreads;  // K chunks per thread (4 or 8)
-  constexpr int VCH = KC / 8;               // V d-chunk rounds per thread (1 or 2)
-  constexpr int NKK = D / 16;
-  constexpr int ND = D / 32;
+  constexpr int NCH = kBN * KC / kThreads;  // chunks per thread of a K (or V) tile: 2 or 4
+  constexpr int NKK = D / 32;               // k-steps of the S MFMA
+  constexpr int ND = D / 16;                // 16-dim subtiles of O
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::kTotal];
+  unsigned char* const ks_lds = smem;
+  unsigned char* const vs_lds = smem + S::kKBytes;
   uint32_t* mask = reinterpret_cast<uint32_t*>(smem + S::kMaskOff);
 
-  const int64_t bh = blockIdx.y;
-  const int f = blockIdx.x;  // flat entry
+  // XCD-aware: consecutive flat entries of a head run on one XCD, so the K/V
+  // blocks they share stay in that XCD's L2
+  const int total = p.n_flat * p.BH;
+  const int per_xcd = (total + 7) / 8;
+  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lid >= total) return;  // whole workgroup, before any barrier
+  const int64_t bh = lid / p.n_flat;
+  const int f = lid % p.n_flat;  // flat entry
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int q = lane & 15;
+  const int g = lane >> 4;
   const int n_kv = p.n_kv;
   const int n_ns = p.n_ns;
   const int32_t* tab = p.kv_tab + bh * n_kv;
@@ -66,17 +88,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
   __syncthreads();
   for (int t = tid; t < n_ns; t += kThreads) atomicOr(&mask[ns[t] >> 5], 1u << (ns[t] & 31));
 
-  // ---- this wave's 32 query rows ----
+  // ---- this wave's 16 query rows; lane (q, g) holds dims 32 kk + 8 g .. + 7 ----
   const int qblk = p.flat[bh * p.n_flat + f];
   // the tail rows of a partial query block read its first row and are not stored
-  const int qr = wave * 32 + l32;
+  const int qr = wave * 16 + q;
   const bool q_ok = qr < p.grid.rows(qblk);
   const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
-    qreg[kk] = *reinterpret_cast<const bf16x8_t*>(Qh + qrow * D + 16 * kk + 8 * hi);
+    qreg[kk] = *reinterpret_cast<const bf16x8_t*>(Qh + qrow * D + 32 * kk + 8 * g);
 
   const bf16_bits* Kh = static_cast<const bf16_bits*>(p.k) + bh * p.kv_head_stride;
   const bf16_bits* Vh = static_cast<const bf16_bits*>(p.v) + bh * p.kv_head_stride;
@@ -104,85 +126,63 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
   const float w0 = src_tail ? log2f((float)src_tail / kBN) / p.scale_log2 : 0.0f;
   const float w1 = ctx_tail ? log2f((float)ctx_tail / kBN) / p.scale_log2 : 0.0f;
 
-  u32x4 kst[KCH];
-  u32x4 vst[4 * VCH];
-  // V^T staging: key group vg = tid % 16 (4 keys), d chunk vd = tid / 16 + 8 c
-  const int vg = tid % (kBN / 4);
-  const int vd0 = tid / (kBN / 4);
-  const int vq = vg & 3;
-  const int vpos = (vg >> 2) * 16 + (((vq & 1) << 1) | (vq >> 1)) * 4;
-
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const bool exact = t < n_ns;
-    const bf16_bits* kb = exact ? Kh : Kch;
-    const bf16_bits* vb = exact ? Vh : Vch;
+  // staging: chunk c = tid + 256 i is row c / KC, 16-byte column c % KC (KC
+  // consecutive threads read one row); K and V are both plain row-major copies
+  u32x4 st[NCH];
+  auto load_rows = [&](int t, const bf16_bits* full, const bf16_bits* pooled)
+      __attribute__((always_inline)) {
+    const bf16_bits* b = t < n_ns ? full : pooled;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + kThreads * i;
-      kst[i] = *reinterpret_cast<const u32x4*>(kb + src_row(t, c / KC) * D + (c % KC) * 8);
+      st[i] = *reinterpret_cast<const u32x4*>(b + src_row(t, c / KC) * D + (c % KC) * 8);
     }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vst[4 * c + r] = *reinterpret_cast<const u32x4*>(
-            vb + src_row(t, 4 * vg + r) * D + (vd0 + 8 * c) * 8);
   };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-    unsigned char* ks = smem + buf * S::kStage;
-    unsigned char* vs = ks + S::kKBytes;
+  auto store_rows = [&](unsigned char* dst, int stride) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(ks + (c / KC) * S::kKStride + (c % KC) * 16) = kst[i];
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      unsigned char* vrow = vs + ((vd0 + 8 * c) * 8) * S::kVStride + vpos * 2;
-      const u32x4 a = vst[4 * c], b = vst[4 * c + 1], d2 = vst[4 * c + 2], d3 = vst[4 * c + 3];
-      // word w of a key's 8 dims holds dims 2w (low half) and 2w+1 (high half)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        *reinterpret_cast<uint2*>(vrow + (2 * w) * S::kVStride) =
-            make_uint2(pack2(a[w], b[w], false), pack2(d2[w], d3[w], false));
-        *reinterpret_cast<uint2*>(vrow + (2 * w + 1) * S::kVStride) =
-            make_uint2(pack2(a[w], b[w], true), pack2(d2[w], d3[w], true));
-      }
+      *reinterpret_cast<u32x4*>(dst + (c / KC) * stride + (c % KC) * 16) = st[i];
     }
   };
 
-  f32x16_t oacc[ND];
+  f32x4_t oacc[ND];
 #pragma unroll
   for (int j = 0; j < ND; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[j][r] = 0.0f;
+    for (int i = 0; i < 4; ++i) oacc[j][i] = 0.0f;
   float m_run = -INFINITY;
-  float l_run = 0.0f;
+  float l_run = 0.0f;  // this lane's share of the row sum (reduced at the end)
   const float sl2 = p.scale_log2;
   const float exact_bias2 = p.exact_bias_log2;  // -log2(b)
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(0);
-  store_tile(0);
+  // One K and one V buffer: K(t+1) is loaded while S(t) runs and stored once
+  // every wave is past S(t); V(t+1) is loaded while O += V(t) P(t) runs and
+  // stored once every wave is past it.  Each store is published by the next
+  // barrier, before the first read of that buffer.
+  load_rows(0, Kh, Kch);
+  store_rows(ks_lds, S::kKStride);
+  load_rows(0, Vh, Vch);
+  store_rows(vs_lds, S::kVStride);
   __syncthreads();  // also publishes the bitmap
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const unsigned char* ks = smem + buf * S::kStage;
-    const unsigned char* vs = ks + S::kKBytes;
+    const bool more = t + 1 < n_tiles;
     const bool exact = t < n_ns;
+    if (more) load_rows(t + 1, Kh, Kch);
 
-    f32x16_t sacc[2];
+    // S^T subtile s: keys 16 s + 4 g + i of query q
+    f32x4_t sacc[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[s][r] = 0.0f;
+      for (int i = 0; i < 4; ++i) sacc[s4][i] = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            ks + (32 * s + l32) * S::kKStride + (16 * kk + 8 * hi) * 2);
-        sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[s], 0, 0, 0);
+            ks_lds + (16 * s4 + q) * S::kKStride + (32 * kk + 8 * g) * 2);
+        sacc[s4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], sacc[s4], 0, 0, 0);
       }
     }
     // representative tiles: mask rows past n_kv and blocks taken exactly, and
@@ -190,38 +190,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
     if (!exact) {
       const int u0 = (t - n_ns) * kBN;
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int u = u0 + 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (u == pu0) sacc[s][r] += w0;
-          if (u == pu1) sacc[s][r] += w1;
-          if (u >= n_kv || ((mask[u >> 5] >> (u & 31)) & 1u)) sacc[s][r] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int u = u0 + 16 * s4 + 4 * g + i;
+          if (u == pu0) sacc[s4][i] += w0;
+          if (u == pu1) sacc[s4][i] += w1;
+          if (u >= n_kv || ((mask[u >> 5] >> (u & 31)) & 1u)) sacc[s4][i] = -INFINITY;
         }
     } else {
       const int pos = ns[t];
       const int vt = (pos == pu0) ? src_tail : ((pos == pu1) ? ctx_tail : kBN);
       if (vt < kBN) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * s + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= vt) sacc[s][r] = -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i)
+            if (16 * s4 + 4 * g + i >= vt) sacc[s4][i] = -INFINITY;
       }
     }
     const float bias2 = exact ? exact_bias2 : 0.0f;
 
+    // row max over the tile: 16 values here, then across the four lane groups
     float tmax = sacc[0][0];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[s][r]);
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[s4][i]);
     {
-      const uint32_t u = __float_as_uint(tmax);
-      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // each swap returns {own, partner} in an order that depends on the lane's
+      // row of 16 (or half of 32), so take both
+      uint32_t u = __float_as_uint(tmax);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      tmax = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      u = __float_as_uint(tmax);
+      const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      tmax = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     }
     const float tmax_s = fmaf(tmax, sl2, bias2);  // -inf for a fully masked tile
     if (__builtin_amdgcn_ballot_w64(tmax_s > m_run + kRescaleThreshold) != 0) {
@@ -231,62 +235,78 @@ __global__ __launch_bounds__(kThreads, 1) void attn_flat_bf16_kernel(FlatParams 
 #pragma unroll
       for (int j = 0; j < ND; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[j][r] *= alpha;
+        for (int i = 0; i < 4; ++i) oacc[j][i] *= alpha;
       m_run = m_new;
     }
     const float off = bias2 - m_run;
-    bf16x8_t pk[4];
+    // P^T operand of chunk c: slots 0-3 = subtile 2c, slots 4-7 = subtile 2c + 1
+    bf16x8_t pk[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int e2 = 0; e2 < 8; e2 += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e2], sl2, off));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e2 + 1], sl2, off));
-        bf16x2_t pr;
-        pr[0] = (__bf16)p0;
-        pr[1] = (__bf16)p1;
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-        pk[c][e2] = pr[0];
-        pk[c][e2 + 1] = pr[1];
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          bf16x2_t pr;
+          pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * c + h][i], sl2, off));
+          pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * c + h][i + 1], sl2, off));
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+          pk[c][4 * h + i] = pr[0];
+          pk[c][4 * h + i + 1] = pr[1];
+        }
       }
     }
+    __syncthreads();  // every wave is past S(t): K may be overwritten
+    if (more) {
+      store_rows(ks_lds, S::kKStride);
+      load_rows(t + 1, Vh, Vch);
+    }
+    // O^T subtile j (dims 16 j + 4 g + i of query q) += V^T P^T; the V^T operand
+    // of chunk c is two transposing reads: keys 32 c + 4 g + (0..3) and
+    // 32 c + 16 + 4 g + (0..3) at dims 16 j .. 16 j + 15 (lane q of a group
+    // addresses key row q / 4, dims 4 (q % 4) .. + 3 of its four-key group)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int j = 0; j < ND; ++j) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            vs + (32 * j + l32) * S::kVStride + (16 * c + 8 * hi) * 2);
-        oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[j], 0, 0, 0);
+        const unsigned char* base =
+            vs_lds + (32 * c + 4 * g + (q >> 2)) * S::kVStride + (16 * j + 4 * (q & 3)) * 2;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)base);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(base + 16 * S::kVStride));
+        const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[c], oacc[j], 0, 0, 0);
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+    __syncthreads();  // every wave is past O += V(t) P(t); K(t+1) is visible
+    if (more) store_rows(vs_lds, S::kVStride);
   }
 
   // ---- epilogue: O / l, bf16 round-to-nearest-even, LSE (+ ln b) ----
   {
-    const uint32_t u = __float_as_uint(l_run);
-    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    uint32_t u = __float_as_uint(l_run);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    l_run = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);  // own + partner
+    u = __float_as_uint(l_run);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    l_run = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
   }
   const float inv = 1.0f / l_run;
   bf16_bits* Oh = static_cast<bf16_bits*>(p.o) + bh * p.q_head_stride + qrow * D;
 #pragma unroll
   for (int j = 0; j < ND && q_ok; ++j) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x2_t a, b;
-      a[0] = (__bf16)(oacc[j][4 * g + 0] * inv);
-      a[1] = (__bf16)(oacc[j][4 * g + 1] * inv);
-      b[0] = (__bf16)(oacc[j][4 * g + 2] * inv);
-      b[1] = (__bf16)(oacc[j][4 * g + 3] * inv);
-      uint2 w;
-      w.x = __builtin_bit_cast(uint32_t, a);
-      w.y = __builtin_bit_cast(uint32_t, b);
-      *reinterpret_cast<uint2*>(Oh + 32 * j + 8 * g + 4 * hi) = w;
-    }
+    bf16x2_t a, b;
+    a[0] = (__bf16)(oacc[j][0] * inv);
+    a[1] = (__bf16)(oacc[j][1] * inv);
+    b[0] = (__bf16)(oacc[j][2] * inv);
+    b[1] = (__bf16)(oacc[j][3] * inv);
+    uint2 w;
+    w.x = __builtin_bit_cast(uint32_t, a);
+    w.y = __builtin_bit_cast(uint32_t, b);
+    *reinterpret_cast<uint2*>(Oh + 16 * j + 4 * g) = w;
   }
-  if (p.lse && hi == 0 && q_ok) {
+  if (p.lse && g == 0 && q_ok) {
     p.lse[bh * p.lse_head_stride + qrow] =
         (m_run + __log2f(l_run)) * 0.69314718055994531f + p.lse_offset;
   }
@@ -402,10 +422,12 @@ hipError_t launch_attention_flat(const FlatParams& p, isa_dtype_t dtype, hipStre
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)p.n_flat, (unsigned)p.BH);
   if (dtype == ISA_DTYPE_BF16) {
+    const int64_t total = (int64_t)p.n_flat * p.BH;
+    const dim3 grid1((unsigned)(((total + 7) / 8) * 8));
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_flat_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL(attn_flat_bf16_kernel<128>, grid1, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(attn_flat_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL(attn_flat_bf16_kernel<64>, grid1, dim3(kThreads), 0, stream, p);
   } else {
     if (p.D == 128)
       hipLaunchKernelGGL(attn_flat_f32_kernel<128>, grid, dim3(kF32Threads), 0, stream, p);
