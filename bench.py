@@ -359,7 +359,7 @@ def sweep(args):
                       "rows": rows}), flush=True)
 
 
-def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_pp_kernel<128>"):
+def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_pp_kernel<128, 1>"):
     """Traffic file text: per-launch HBM bytes of `kernel`, from rocprofv3
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on
     the 256 MiB copy of --calibrate-copy (268435456 bytes read and written)."""
@@ -493,7 +493,7 @@ def main():
     pool_bytes = 3.0 * B * H * N * D * 2 + B * H * info["n_q_blocks"] * D * (8 + 8 + 2 + 2)
     ex_ms = stage_ms["attn_exact"]
     achieved = exact_flops / (ex_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_fwd_pp_kernel<128> (exact path)", "bound": "mfma",
+    roofline = {"kernel": "attn_fwd_pp_kernel<128, 1> (exact path)", "bound": "mfma",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                 "algorithmic_flops_per_launch": exact_flops, "avg_launch_ms": ex_ms}

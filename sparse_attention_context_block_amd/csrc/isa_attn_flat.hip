@@ -42,10 +42,11 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D>
 struct FlatSmem {
-  // K rows: 16 lanes read one 16-byte chunk of 16 consecutive rows (stride
-  // 16 mod 256 bytes: all banks).  V rows: a transposing read touches 8 bytes
-  // of 16 rows, 4 per key row (stride 32 mod 256: every 8 rows cover the banks)
-  static constexpr int kKStride = D * 2 + 16;
+  // Row strides measured on gfx950: 16 lanes reading one 16-byte chunk of 16
+  // consecutive rows (the K operand) run conflict-free at 2 D + 32 bytes and
+  // at half rate at 2 D + 16; the transposing V reads run at the same rate
+  // for both.
+  static constexpr int kKStride = D * 2 + 32;
   static constexpr int kVStride = D * 2 + 32;
   static constexpr int kKBytes = kBN * kKStride;
   static constexpr int kVBytes = kBN * kVStride;
