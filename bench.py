@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--rope-steps", type=int, default=10)
     ap.add_argument("--block-lengths", type=int, nargs="*", default=[32, 128],
                     help="also time the forward with these block lengths (none: skip)")
+    ap.add_argument("--dist-reps", type=int, default=30,
+                    help="per-call latency percentiles and cold-cache stage times over this "
+                         "many single calls (0 = skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the workload line: ISA vs dense over N = 5K..64K")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -99,6 +102,73 @@ def cpu_baseline(inp, c, n_heads):
             "latency_ms_extrapolated": per_job_s * 1e3,
             "sample": f"isa_ref (fp64 NumPy) on {n_heads} of {B * H} heads of the same input, "
                       f"{dt:.1f} s, extrapolated linearly to all heads"}
+
+
+def _pcts(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(xs)), "p10": float(np.percentile(xs, 10)),
+            "p90": float(np.percentile(xs, 90)), "n": int(xs.size)}
+
+
+def per_call_ms(torch, fn, reps, before=None):
+    """Event time of each of reps single calls of fn; before() runs untimed ahead of each."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if before is not None:
+            before()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_distribution(args, isa, torch, plan, q, k, v, o, lse, ws, dev, with_dense):
+    """Per-call latency of the forward (and the dense kernel), warm, and the
+    forward's stage times with the caches cold: a 1 GiB write between calls
+    evicts the L2s and the 256 MB MALL, so every input comes from HBM."""
+    reps = args.dist_reps
+    out = {"reps": reps}
+    out["isa_warm_ms"] = _pcts(per_call_ms(
+        torch, lambda: isa.isa_forward(plan, q, k, v, o, lse, workspace=ws), reps))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    tick = [0]
+
+    def evict():
+        tick[0] += 1
+        flush.fill_(tick[0] & 0xFF)
+
+    out["isa_cold_ms"] = _pcts(per_call_ms(
+        torch, lambda: isa.isa_forward(plan, q, k, v, o, lse, workspace=ws), reps, before=evict))
+    n_ev = isa.ISA_PROFILE_STAGES + 1
+    stage = {"warm": [], "cold": []}
+    for kind in ("warm", "cold"):
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(reps)]
+        for evs in events:
+            for ev in evs:
+                ev.record()
+        torch.cuda.synchronize()
+        for evs in events:
+            if kind == "cold":
+                evict()
+            isa.isa_forward(plan, q, k, v, o, lse, workspace=ws, events=evs)
+        torch.cuda.synchronize()
+        stage[kind] = {name: float(np.median([evs[j].elapsed_time(evs[j + 1]) for evs in events]))
+                       for j, name in enumerate(isa.STAGE_NAMES)}
+    out["stages_warm_median_ms"] = stage["warm"]
+    out["stages_cold_median_ms"] = stage["cold"]
+    out["flush_bytes"] = int(flush.numel())
+    del flush
+    if with_dense:
+        od, lsed = torch.empty_like(q), torch.empty_like(lse)
+        out["dense_warm_ms"] = _pcts(per_call_ms(
+            torch, lambda: isa.isa_dense_forward(q, k, v, od, lsed), max(reps // 3, 5)))
+        del od, lsed
+    _log(f"per-call ISA warm {out['isa_warm_ms']}, cold {out['isa_cold_ms']}")
+    _log(f"stages cold {stage['cold']}")
+    return out
 
 
 def kernel_source_sha256():
@@ -487,6 +557,11 @@ def main():
         _log(f"dense {dms:.3f} ms")
         del od, lsed
 
+    dist = None
+    if args.dist_reps > 0:
+        dist = bench_distribution(args, isa, torch, plan, q, k, v, o, lse, ws, dev,
+                                  not args.no_dense)
+
     dense_equiv = 4.0 * B * H * N * N * D
     exact_flops = 4.0 * B * H * info["n_sharp"] * b * info["l_new"] * D
     taylor_flops = 4.0 * B * H * info["n_flat"] * b * info["n_kv_blocks"] * D
@@ -528,6 +603,7 @@ def main():
         "stages": stages,
         "dense_baseline": dense,
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
+        "latency_distribution": dist,
         "roofline": roofline,
         "block_mask": block_mask,
         "rope": rope,

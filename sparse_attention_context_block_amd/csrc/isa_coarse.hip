@@ -13,171 +13,201 @@
 //             With alpha_ns > 0 it also stores every x_ij (fp64), which the
 //             block mask of the flat query blocks ranks.
 //   colsum:   per context block j, c_j = mean over source query blocks i of
-//             S_coarse[i, n_src + j] ([notes] key design 1), reduced in a fixed
-//             order (no atomics), so the result is deterministic.
+//             S_coarse[i, n_src + j] ([notes] key design 1).
 //
-// Both kernels tile x as a small fp64 GEMM: 32 query blocks x 32 key blocks
-// per step, operands staged transposed in LDS, 2x2 outputs per thread.
+// Both kernels form x in 16 x 16 tiles with v_mfma_f64_16x16x4_f64.  A lane
+// (q, g) (q = lane % 16, g = lane / 16) holds dims (D/4) g .. (D/4) g + D/4 - 1
+// of one row of each operand, so step s of a tile multiplies dims (D/4) g + s
+// of row q of A and column q of B, and the D/4 steps together sum all D dims.
+// The lane then holds x[g + 4 r][q] in register r of the tile (this fp64 MFMA
+// spreads the output rows over the lane groups first, unlike the 32-bit ones,
+// whose register r of lane group g holds row 4 g + r).  The operands
+// come straight from global memory as contiguous runs of D/4 doubles; nothing
+// is staged in LDS.  A workgroup's four waves split the tiles of one 16-row
+// (rowstats) or 16-column (colsum) strip four ways; their partial results are
+// combined in a fixed order (no atomics), so every result is deterministic.
 #include "isa_internal.h"
 
 namespace isa {
 namespace {
 
-constexpr int kT = 32;         // tile edge (rows and columns)
-constexpr int kThreads = 256;  // 16 x 16 threads, 2 x 2 outputs each
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-// Stage rows [r0, r0 + kT) of src ([n][D] fp64) transposed into dst[D][kT];
-// rows outside [0, n) are zero.
+constexpr int kThreads = 256;  // four waves
+constexpr int kTile = 16;
+
+// One lane's part of a 16-row operand tile: row `row` of base ([n][D], n >= 1),
+// dims (D/4) g .. + D/4 - 1.  Rows past the end read row n - 1: the results
+// they feed are never used.  The load is unconditional, so the wait for one
+// operand buffer never includes the other buffer's loads.
 template <int D>
-__device__ inline void stage_transposed(double (*dst)[kT], const double* __restrict__ src,
-                                        int r0, int n) {
-  constexpr int kPairs = kT * D / 2;
-  for (int i = threadIdx.x; i < kPairs; i += kThreads) {
-    const int r = i / (D / 2);
-    const int d = (i % (D / 2)) * 2;
-    double2 v = make_double2(0.0, 0.0);
-    if (r0 + r < n) v = *reinterpret_cast<const double2*>(src + (int64_t)(r0 + r) * D + d);
-    dst[d][r] = v.x;
-    dst[d + 1][r] = v.y;
+__device__ inline void load_part(double (&v)[D / 4], const double* __restrict__ base, int row,
+                                 int n, int g) {
+  const double2* p =
+      reinterpret_cast<const double2*>(base + (int64_t)min(row, n - 1) * D + (D / 4) * g);
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    const double2 t = p[i];
+    v[2 * i] = t.x;
+    v[2 * i + 1] = t.y;
   }
 }
 
-// acc[a][b] = sum_d QT[d][2*tr + a] * KT[d][2*tc + b]
+// x[g + 4 r][q] = sum_d A[g + 4 r][d] B[q][d] for the lane (q, g)
 template <int D>
-__device__ inline void tile_dot(const double (*QT)[kT], const double (*KT)[kT], int tr, int tc,
-                                double acc[2][2]) {
-  acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = 0.0;
-#pragma unroll 8
-  for (int d = 0; d < D; ++d) {
-    const double2 a = *reinterpret_cast<const double2*>(&QT[d][2 * tr]);
-    const double2 b = *reinterpret_cast<const double2*>(&KT[d][2 * tc]);
-    acc[0][0] = fma(a.x, b.x, acc[0][0]);
-    acc[0][1] = fma(a.x, b.y, acc[0][1]);
-    acc[1][0] = fma(a.y, b.x, acc[1][0]);
-    acc[1][1] = fma(a.y, b.y, acc[1][1]);
-  }
+__device__ inline f64x4_t tile_dot(const double (&a)[D / 4], const double (&b)[D / 4]) {
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < D / 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc, 0, 0, 0);
+  return acc;
 }
 
+// Online (max, sum e^{x-m}, sum e^{2(x-m)}) of one row.
+struct RowStat {
+  double m, l, s2;
+};
+
+__device__ inline void stat_add(RowStat& st, double x) {
+  if (x > st.m) {
+    const double f = exp(st.m - x);  // 0 when m is -inf
+    st.l *= f;
+    st.s2 *= f * f;
+    st.m = x;
+  }
+  const double e = exp(x - st.m);
+  st.l += e;
+  st.s2 += e * e;
+}
+
+__device__ inline RowStat stat_merge(const RowStat& a, const RowStat& b) {
+  const double mn = fmax(a.m, b.m);
+  const double fa = (a.m == -INFINITY) ? 0.0 : exp(a.m - mn);
+  const double fb = (b.m == -INFINITY) ? 0.0 : exp(b.m - mn);
+  return {mn, a.l * fa + b.l * fb, a.s2 * fa * fa + b.s2 * fb * fb};
+}
+
+// One workgroup = 16 query blocks (rows); wave w takes the key tiles t = w,
+// w + 4, ... and keeps per-lane statistics of its rows g, g + 4, g + 8, g + 12.
 template <int D>
-__global__ __launch_bounds__(kThreads) void rowstats_kernel(
+__global__ __launch_bounds__(kThreads, 2) void rowstats_kernel(
     const double* __restrict__ qc, const double* __restrict__ kc, int n_q, double scale,
     double* __restrict__ rowmax, double* __restrict__ rowsum, double* __restrict__ sharpness,
     double* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) double QT[D][kT];
-  __shared__ __attribute__((aligned(16))) double KT[D][kT];
+  __shared__ RowStat part[4][kTile];
   const int64_t bh = blockIdx.y;
-  const int r0 = blockIdx.x * kT;
-  const int tid = threadIdx.x;
-  const int tr = tid / 16, tc = tid % 16;  // a row's 16 threads share one wave
-  const double* q = qc + bh * n_q * (int64_t)D;
-  const double* k = kc + bh * n_q * (int64_t)D;
+  const int r0 = blockIdx.x * kTile;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane & 15, g = lane >> 4;
+  const double* qh = qc + bh * n_q * (int64_t)D;
+  const double* kh = kc + bh * n_q * (int64_t)D;
 
-  stage_transposed<D>(QT, q, r0, n_q);
-  double m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0, 0.0}, s2[2] = {0.0, 0.0};
-  for (int c0 = 0; c0 < n_q; c0 += kT) {
-    __syncthreads();
-    stage_transposed<D>(KT, k, c0, n_q);
-    __syncthreads();
-    double acc[2][2];
-    tile_dot<D>(QT, KT, tr, tc, acc);
+  double a[D / 4];
+  load_part<D>(a, qh, r0 + q, n_q, g);
+  RowStat st[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (c0 + 2 * tc + b >= n_q) continue;
+  for (int r = 0; r < 4; ++r) st[r] = {-INFINITY, 0.0, 0.0};
+
+  const int n_tiles = (n_q + kTile - 1) / kTile;
+  auto consume = [&](const f64x4_t& x, int t) __attribute__((always_inline)) {
+    const int col = t * kTile + q;
+    if (col >= n_q) return;
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const double x = acc[a][b] * scale;
-        if (logits && r0 + 2 * tr + a < n_q)
-          logits[(bh * n_q + r0 + 2 * tr + a) * (int64_t)n_q + c0 + 2 * tc + b] = x;
-        if (x > m[a]) {
-          const double f = exp(m[a] - x);  // 0 when m is -inf
-          l[a] *= f;
-          s2[a] *= f * f;
-          m[a] = x;
-        }
-        const double e = exp(x - m[a]);
-        l[a] += e;
-        s2[a] += e * e;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const double xs = x[r] * scale;
+      const int row = r0 + g + 4 * r;
+      if (logits && row < n_q) logits[(bh * n_q + row) * (int64_t)n_q + col] = xs;
+      stat_add(st[r], xs);
     }
+  };
+  // the next tile's loads are issued as soon as the MFMAs have read the
+  // operand and overlap the exponentials of this tile; the second wave on the
+  // SIMD covers the rest of their latency (tile indices past the last tile are
+  // clamped, and nothing reads the last load)
+  double b[D / 4];
+  const int last = n_tiles - 1;
+  load_part<D>(b, kh, min(wave, last) * kTile + q, n_q, g);
+  for (int t = wave; t < n_tiles; t += 4) {
+    const f64x4_t x = tile_dot<D>(a, b);
+    load_part<D>(b, kh, min(t + 4, last) * kTile + q, n_q, g);
+    consume(x, t);
   }
-  // combine the 16 column threads of each row (lanes differing in bits 0..3)
+  // merge the 16 column lanes of each row (lanes differing in bits 0..3)
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+  for (int r = 0; r < 4; ++r) {
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
-      const double mo = __shfl_xor(m[a], off);
-      const double lo = __shfl_xor(l[a], off);
-      const double so = __shfl_xor(s2[a], off);
-      const double mn = fmax(m[a], mo);
-      const double fa = (m[a] == -INFINITY) ? 0.0 : exp(m[a] - mn);
-      const double fb = (mo == -INFINITY) ? 0.0 : exp(mo - mn);
-      l[a] = l[a] * fa + lo * fb;
-      s2[a] = s2[a] * fa * fa + so * fb * fb;
-      m[a] = mn;
+      const RowStat o = {__shfl_xor(st[r].m, off), __shfl_xor(st[r].l, off),
+                         __shfl_xor(st[r].s2, off)};
+      st[r] = stat_merge(st[r], o);
     }
   }
-  if (tc == 0) {
-    const double nk = (double)n_q;
+  if (q == 0) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int r = r0 + 2 * tr + a;
-      if (r >= n_q) continue;
-      const int64_t o = bh * n_q + r;
-      rowmax[o] = m[a];
-      rowsum[o] = l[a];
-      const double num = nk * s2[a] - l[a] * l[a];
-      sharpness[o] = num / (nk * nk * l[a] * l[a]);
+    for (int r = 0; r < 4; ++r) part[wave][g + 4 * r] = st[r];
+  }
+  __syncthreads();
+  if (threadIdx.x < kTile) {
+    const int row = r0 + threadIdx.x;
+    if (row < n_q) {
+      RowStat s = part[0][threadIdx.x];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) s = stat_merge(s, part[w][threadIdx.x]);  // fixed order
+      const double nk = (double)n_q;
+      const int64_t o = bh * n_q + row;
+      rowmax[o] = s.m;
+      rowsum[o] = s.l;
+      sharpness[o] = (nk * s.s2 - s.l * s.l) / (nk * nk * s.l * s.l);
     }
   }
 }
 
+// One workgroup = 16 context blocks (columns); wave w takes the source row
+// tiles t = w, w + 4, ...; lane (q, g) sums the probabilities of its rows
+// g, g + 4, g + 8, g + 12 into column q.
 template <int D>
-__global__ __launch_bounds__(kThreads) void colsum_kernel(
+__global__ __launch_bounds__(kThreads, 2) void colsum_kernel(
     const double* __restrict__ qc, const double* __restrict__ kc,
     const double* __restrict__ rowmax, const double* __restrict__ rowsum, int n_q, int n_src,
     int n_ctx, double scale, double* __restrict__ ctx_score) {
-  __shared__ __attribute__((aligned(16))) double QT[D][kT];
-  __shared__ __attribute__((aligned(16))) double KT[D][kT];
-  __shared__ double mrow[kT], inv_lrow[kT];
-  __shared__ double part[kThreads / 16][kT];
+  __shared__ double part[4][kTile];
   const int64_t bh = blockIdx.y;
-  const int c0 = blockIdx.x * kT;  // context column tile
-  const int tid = threadIdx.x;
-  const int tr = tid / 16, tc = tid % 16;
-  const double* q = qc + bh * n_q * (int64_t)D;
-  const double* k = kc + (bh * n_q + n_src) * (int64_t)D;
+  const int c0 = blockIdx.x * kTile;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane & 15, g = lane >> 4;
+  const double* qh = qc + bh * n_q * (int64_t)D;
+  const double* kh = kc + (bh * n_q + n_src) * (int64_t)D;
+  const double* mh = rowmax + bh * n_q;
+  const double* lh = rowsum + bh * n_q;
 
-  stage_transposed<D>(KT, k, c0, n_ctx);
-  double colacc[2] = {0.0, 0.0};
-  for (int r0 = 0; r0 < n_src; r0 += kT) {
-    __syncthreads();
-    stage_transposed<D>(QT, q, r0, n_src);
-    if (tid < kT) {
-      const int r = r0 + tid;
-      mrow[tid] = r < n_src ? rowmax[bh * n_q + r] : 0.0;
-      inv_lrow[tid] = r < n_src ? 1.0 / rowsum[bh * n_q + r] : 0.0;
-    }
-    __syncthreads();
-    double acc[2][2];
-    tile_dot<D>(QT, KT, tr, tc, acc);
+  double bcol[D / 4];
+  load_part<D>(bcol, kh, c0 + q, n_ctx, g);
+  double colacc = 0.0;
+  const int n_tiles = (n_src + kTile - 1) / kTile;
+  auto consume = [&](const f64x4_t& x, int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int rl = 2 * tr + a;
-      if (r0 + rl >= n_src) continue;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        colacc[b] += exp(acc[a][b] * scale - mrow[rl]) * inv_lrow[rl];
+    for (int r = 0; r < 4; ++r) {
+      const int row = t * kTile + g + 4 * r;
+      if (row < n_src) colacc += exp(x[r] * scale - mh[row]) / lh[row];
     }
+  };
+  double a[D / 4];
+  const int last = n_tiles - 1;
+  load_part<D>(a, qh, min(wave, last) * kTile + q, n_src, g);
+  for (int t = wave; t < n_tiles; t += 4) {
+    const f64x4_t x = tile_dot<D>(a, bcol);
+    load_part<D>(a, qh, min(t + 4, last) * kTile + q, n_src, g);
+    consume(x, t);
   }
-  part[tr][2 * tc] = colacc[0];
-  part[tr][2 * tc + 1] = colacc[1];
+  // column q: the four lane groups in order, then the four waves in order
+  colacc += __shfl_xor(colacc, 16);
+  colacc += __shfl_xor(colacc, 32);
+  if (g == 0) part[wave][q] = colacc;
   __syncthreads();
-  if (tid < kT) {
-    const int j = c0 + tid;
+  if (threadIdx.x < kTile) {
+    const int j = c0 + threadIdx.x;
     if (j < n_ctx) {
-      double s = 0.0;
-#pragma unroll
-      for (int g = 0; g < kThreads / 16; ++g) s += part[g][tid];  // fixed order
+      const double s = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                       part[3][threadIdx.x];
       ctx_score[bh * n_ctx + j] = s / (double)n_src;
     }
   }
@@ -189,7 +219,7 @@ hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, in
                                   double* rowmax, double* rowsum, double* sharpness,
                                   double* logits, hipStream_t stream) {
   if (BH == 0 || n_q == 0) return hipSuccess;
-  dim3 grid((n_q + kT - 1) / kT, BH);
+  dim3 grid((n_q + kTile - 1) / kTile, BH);
   const double scale = 1.0 / sqrt((double)D);
   if (D == 128)
     hipLaunchKernelGGL(rowstats_kernel<128>, grid, dim3(kThreads), 0, stream, qc, kc, n_q, scale,
@@ -204,7 +234,7 @@ hipError_t launch_coarse_colsum(const double* qc, const double* kc, const double
                                 const double* rowsum, int BH, int n_q, int n_src, int n_ctx,
                                 int D, double* ctx_score, hipStream_t stream) {
   if (BH == 0 || n_ctx == 0 || n_src == 0) return hipSuccess;
-  dim3 grid((n_ctx + kT - 1) / kT, BH);
+  dim3 grid((n_ctx + kTile - 1) / kTile, BH);
   const double scale = 1.0 / sqrt((double)D);
   if (D == 128)
     hipLaunchKernelGGL(colsum_kernel<128>, grid, dim3(kThreads), 0, stream, qc, kc, rowmax,
