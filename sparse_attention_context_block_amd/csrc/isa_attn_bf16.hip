@@ -35,6 +35,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBN = 64;          // keys per tile
+// Row tables up to this length are copied into LDS once per workgroup, so a
+// tile's row lookups cost an LDS read instead of a global round trip ahead of
+// its data loads (8 KB: two workgroups per CU still fit).
+constexpr int kTabLds = 2048;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 template <int D>
@@ -47,8 +51,11 @@ struct Smem {
   static constexpr int kTotal = 2 * kStage;
 };
 
-template <int D, bool kRowTable>
+// kSrc: 0 = block table, 1 = row table read from global memory, 2 = row
+// table copied into LDS (at most kTabLds rows)
+template <int D, int kSrc>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p) {
+  constexpr bool kRowTable = kSrc != 0;
   using S = Smem<D>;
   constexpr int KC = D / 8;      // 16-byte chunks per K row
   constexpr int KCH = kBN * KC / kThreads;  // K chunks per thread per tile (2 or 4)
@@ -56,6 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   constexpr int NKK = D / 16;    // k-steps of the S MFMA
   constexpr int ND = D / 32;     // d subtiles of O
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::kTotal];
+  __shared__ int32_t tab_s[kSrc == 2 ? kTabLds : 1];
 
   // ---- XCD-aware mapping of workgroups to (head, query tile) ----
   const int wg_per_head = (p.n_q_entries + 1) / 2;
@@ -107,7 +115,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
       const Slice& sl = (r & 32) ? sl_b : sl_a;
       return (int64_t)sl.start + min(r & 31, max(sl.cnt - 1, 0));
     }
-    return tab[min(t * kBN + r, p.kv_rows - 1)];  // rows past the end: valid, then masked
+    const int u = min(t * kBN + r, p.kv_rows - 1);  // rows past the end: valid, then masked
+    return kSrc == 2 ? tab_s[u] : tab[u];
   };
   // Row table (pooled rows): the partial blocks' rows (the source tail at K_new
   // position n_src - 1, the context tail last if kept) carry the weight
@@ -202,6 +211,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnParams p
   const float sl2 = p.scale_log2;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  if constexpr (kSrc == 2) {
+    for (int i = tid; i < p.kv_rows; i += kThreads) tab_s[i] = tab[i];
+    __syncthreads();
+  }
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -359,17 +372,19 @@ hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(((total + 7) / 8) * 8));
   const bool row_table = p.kv_row_table != 0;
   if (!row_table && p.kv_rows % 32 != 0) return hipErrorInvalidValue;
+  const int src = !row_table ? 0 : (p.kv_rows <= kTabLds ? 2 : 1);
+#define ISA_BF16_LAUNCH(DD, SRC) \
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, SRC>), grid, dim3(kThreads), 0, stream, p)
   if (p.D == 128) {
-    if (row_table)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, dim3(kThreads), 0, stream, p);
+    if (src == 2) ISA_BF16_LAUNCH(128, 2);
+    else if (src == 1) ISA_BF16_LAUNCH(128, 1);
+    else ISA_BF16_LAUNCH(128, 0);
   } else {
-    if (row_table)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, dim3(kThreads), 0, stream, p);
+    if (src == 2) ISA_BF16_LAUNCH(64, 2);
+    else if (src == 1) ISA_BF16_LAUNCH(64, 1);
+    else ISA_BF16_LAUNCH(64, 0);
   }
+#undef ISA_BF16_LAUNCH
   return hipGetLastError();
 }
 
