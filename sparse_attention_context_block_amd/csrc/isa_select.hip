@@ -30,26 +30,26 @@ __device__ inline uint64_t order_key(double x) {
 }
 
 // Writes the indices i < n with flag[i] != 0 to ones (ascending) and, if zeros
-// is non-null, the others to zeros (ascending).
+// is non-null, the others to zeros (ascending).  Thread t owns a contiguous
+// run of the flags; the exclusive prefix of the runs' counts comes from a
+// shuffle scan inside each wave plus the totals of the lower waves.
 __device__ void compact(const uint8_t* flag, int n, int32_t* ones, int32_t* zeros,
                         int32_t* counts) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + kThreads - 1) / kThreads;
   const int b = min(tid * per, n), e = min(b + per, n);
   int c = 0;
   for (int i = b; i < e; ++i) c += flag[i] ? 1 : 0;
-  counts[tid] = c;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int x = counts[t];
-      counts[t] = run;
-      run += x;
-    }
+  int incl = c;  // inclusive scan over the lanes of this wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) counts[wave] = incl;
   __syncthreads();
-  int o1 = counts[tid];
+  int o1 = incl - c;
+  for (int w = 0; w < wave; ++w) o1 += counts[w];
   int o0 = b - o1;  // zeros before b
   for (int i = b; i < e; ++i) {
     if (flag[i])
@@ -107,6 +107,9 @@ __global__ __launch_bounds__(kThreads) void select_route_kernel(
   compact(flag, n_q, flat + bh * n_flat, sharp + bh * (int64_t)(n_q - n_flat), counts);
 }
 
+// Byte offset of the per-wave counts after key[n] (8 bytes each) and flag[n].
+__host__ __device__ inline int ns_counts_offset(int n) { return (9 * n + 15) & ~15; }
+
 // Block mask of one flat query block i ([notes] key design 2; the mask is
 // read off the coarse map, [summary] 2 "Pooling Attention"): rank the n_kv
 // blocks of K_new by x_i,kv_tab[u] (descending; the coarse probability is
@@ -116,10 +119,11 @@ __global__ __launch_bounds__(kThreads) void ns_select_kernel(
     const double* __restrict__ logits, const int32_t* __restrict__ flat,
     const int32_t* __restrict__ kv_tab, int n_q, int n_flat, int n_kv, int n_ns,
     int32_t* __restrict__ ns) {
+  // LDS sized by n_kv at launch (a few KB), so many workgroups share a CU
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* key = reinterpret_cast<uint64_t*>(smem);                // [n_kv]
-  uint8_t* flag = smem + sizeof(uint64_t) * kMaxBlocksPerHead;      // [n_kv]
-  int32_t* counts = reinterpret_cast<int32_t*>(flag + kMaxBlocksPerHead);  // [kThreads]
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem);                     // [n_kv]
+  uint8_t* flag = smem + sizeof(uint64_t) * n_kv;                        // [n_kv]
+  int32_t* counts = reinterpret_cast<int32_t*>(smem + ns_counts_offset(n_kv));  // [waves]
   const int f = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int tid = threadIdx.x;
@@ -148,8 +152,7 @@ hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int
                             hipStream_t stream) {
   if (BH == 0 || n_flat == 0 || n_ns == 0) return hipSuccess;
   if (n_kv < 1 || n_kv > kMaxBlocksPerHead || n_ns > n_kv) return hipErrorInvalidValue;
-  const size_t lds = sizeof(uint64_t) * kMaxBlocksPerHead + kMaxBlocksPerHead +
-                     sizeof(int32_t) * kThreads;
+  const size_t lds = ns_counts_offset(n_kv) + sizeof(int32_t) * (kThreads / 64);
   hipLaunchKernelGGL(ns_select_kernel, dim3(n_flat, BH), dim3(kThreads), lds, stream, logits,
                      flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
   return hipGetLastError();
