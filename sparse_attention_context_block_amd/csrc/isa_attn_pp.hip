@@ -96,16 +96,56 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   const int32_t* tab = p.kv_tab ? p.kv_tab + bh * p.kv_tab_stride : nullptr;
   const int kv_slices = p.kv_rows / 32;
   const int n_tiles = (kv_slices + 1) / 2;
-  // the two slices of tile u; keys past a slice's valid rows (partial blocks,
-  // an odd slice count) are masked
+  const int last = n_tiles - 1;
+  // The block grid stays in scalar registers (left alone, the compiler reloads
+  // its fields from the kernel arguments on every tile, each load waited on at
+  // once).
+  BlockGrid g;
+  g.L_src = __builtin_amdgcn_readfirstlane(p.grid.L_src);
+  g.n_src = __builtin_amdgcn_readfirstlane(p.grid.n_src);
+  g.N = __builtin_amdgcn_readfirstlane(p.grid.N);
+  g.len = __builtin_amdgcn_readfirstlane(p.grid.len);
+  asm("" : "+s"(g.L_src), "+s"(g.n_src), "+s"(g.N), "+s"(g.len));
+  // The two slices of tile u (keys past a slice's valid rows, of partial blocks
+  // or past an odd slice count, are masked), as the block ids read from the
+  // table (TileIds) and as their rows (TileSrc).  Ids are read one iteration
+  // before they are decoded, so no tile waits on a table read.
   struct TileSrc {
     Slice a, b;
   };
-  auto tile_src = [&](int u) -> TileSrc {
+  struct TileIds {
+    int a, b;
+  };
+  auto tile_ids = [&](int u) -> TileIds {
+    if constexpr (kShift == 0) {  // one block per slice
+      const int ea = 2 * u, eb = min(2 * u + 1, kv_slices - 1);
+      return {tab ? tab[ea] : ea, tab ? tab[eb] : eb};
+    } else {  // both slices in block u >> (kShift - 1)
+      const int e = u >> (kShift - 1);
+      const int blk = tab ? tab[e] : e;
+      return {blk, blk};
+    }
+  };
+  auto decode = [&](TileIds id, int u) -> TileSrc {
     TileSrc ts;
-    tile_slices<kShift>(p.grid, tab, kv_slices, u, ts.a, ts.b);
+    if constexpr (kShift == 0) {
+      ts.a = Slice{g.start(id.a), min(g.rows(id.a), 32)};
+      ts.b = 2 * u + 1 < kv_slices ? Slice{g.start(id.b), min(g.rows(id.b), 32)} : Slice{0, 0};
+    } else {
+      const int sub = (u & ((1 << (kShift - 1)) - 1)) * 2;
+      const int st = g.start(id.a), rows = g.rows(id.a);
+      const int ca = min(max(rows - 32 * sub, 0), 32);
+      const int cb = min(max(rows - 32 * (sub + 1), 0), 32);
+      ts.a = Slice{ca > 0 ? st + 32 * sub : st, ca};
+      ts.b = Slice{cb > 0 ? st + 32 * (sub + 1) : st, cb};
+    }
+    ts.a.start = __builtin_amdgcn_readfirstlane(ts.a.start);
+    ts.a.cnt = __builtin_amdgcn_readfirstlane(ts.a.cnt);
+    ts.b.start = __builtin_amdgcn_readfirstlane(ts.b.start);
+    ts.b.cnt = __builtin_amdgcn_readfirstlane(ts.b.cnt);
     return ts;
   };
+  auto tile_src = [&](int u) -> TileSrc { return decode(tile_ids(u), u); };
 
   // group A stages K: chunk c = gtid + 256 i -> row c / KC, column chunk c % KC
   uint4 k0, k1, k2, k3;
@@ -212,9 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
     }
   };
   // online softmax of sacc (exp2 domain) into the packed P^T operands
-  auto softmax = [&](int t) __attribute__((always_inline)) {
+  auto softmax = [&](const TileSrc& ts) __attribute__((always_inline)) {
     {
-      const TileSrc ts = tile_src(t);
       if (ts.a.cnt < 32 || ts.b.cnt < 32) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -278,22 +317,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   };
 
   // ---- prologue (phase -1 and phase 0; B also phase 1) ----
-  TileSrc e_next = tile_src(min(1, n_tiles - 1));  // the next tile this group loads
+  // tiles t, t + 1, t + 2 of the loop below, and the ids of tile t + 3
+  TileSrc cur = tile_src(0), n1 = tile_src(min(1, last)), n2 = tile_src(min(2, last));
+  TileIds id3 = tile_ids(min(3, last));
   if (gA) {
-    load_k(tile_src(0));
+    load_k(cur);
     store_k(0);
   } else {
-    load_v(tile_src(0));
+    load_v(cur);
   }
   phase_barrier();                                 // barrier 1
   if (gA) {                                        // phase 0: A computes S(0)
     qk(k_lds(0));
-    if (n_tiles > 1) load_k(e_next);
+    if (n_tiles > 1) load_k(n1);
   } else {                                         // phase 0: B stores V(0)
     store_v(0);
-    if (n_tiles > 1) load_v(e_next);
+    if (n_tiles > 1) load_v(n1);
   }
-  e_next = tile_src(min(2, n_tiles - 1));
   phase_barrier();                                 // barrier 2
   if (!gA) {                                       // phase 1: B computes S(0)
     qk(k_lds(0));
@@ -302,18 +342,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
 
   // ---- main loop: VALU phase, barrier, MFMA phase, barrier ----
   for (int t = 0; t < n_tiles; ++t) {
-    softmax(t);
+    // tile t + 3 from the ids read one iteration ago; read those of tile t + 4
+    const TileSrc n3 = decode(id3, min(t + 3, last));
+    id3 = tile_ids(min(t + 4, last));
+    softmax(cur);
     if (t + 1 < n_tiles) {
-      const TileSrc ent = e_next;
-      e_next = tile_src(min(t + 3, n_tiles - 1));
       if (gA) {
         store_k((t + 1) & 1);
-        if (t + 2 < n_tiles) load_k(ent);
+        if (t + 2 < n_tiles) load_k(n2);
       } else {
         store_v((t + 1) & 1);
-        if (t + 2 < n_tiles) load_v(ent);
+        if (t + 2 < n_tiles) load_v(n2);
       }
     }
+    cur = n1;
+    n1 = n2;
+    n2 = n3;
     // keep the exps of the softmax in this VALU phase: without the fences the
     // scheduler moves them past the barrier into the MFMA phase
     __builtin_amdgcn_sched_barrier(0);
