@@ -54,7 +54,14 @@ struct FlatSmem {
   static constexpr int kTotal = kMaskOff + kMaxBlocksPerHead / 8;
 };
 
-template <int D>
+// Tables up to this many entries (the exact tiles' block ids, then the row
+// table of the representative tiles) are copied into LDS once per workgroup:
+// a tile's row lookups then cost an LDS read instead of dependent scalar or
+// vector loads from global memory, each waited on at once.  896 ints fill the
+// LDS left over with four workgroups per CU.
+constexpr int kLdsTab = 896;
+
+template <int D, bool kTabInLds>
 __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams p) {
   using S = FlatSmem<D>;
   constexpr int KC = D / 8;                 // 16-byte chunks per row
@@ -65,6 +72,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
   unsigned char* const ks_lds = smem;
   unsigned char* const vs_lds = smem + S::kKBytes;
   uint32_t* mask = reinterpret_cast<uint32_t*>(smem + S::kMaskOff);
+  __shared__ int32_t tabs[kTabInLds ? kLdsTab : 1];
 
   // XCD-aware: consecutive flat entries of a head run on one XCD, so the K/V
   // blocks they share stay in that XCD's L2
@@ -83,6 +91,19 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
   const int n_ns = p.n_ns;
   const int32_t* tab = p.kv_tab + bh * n_kv;
   const int32_t* ns = p.ns + (bh * p.n_flat + f) * n_ns;
+  // Loop-invariant scalars pinned in scalar registers (left alone, the compiler
+  // reloads them from the kernel arguments inside the tile loop).
+  BlockGrid gr;
+  gr.L_src = __builtin_amdgcn_readfirstlane(p.grid.L_src);
+  gr.n_src = __builtin_amdgcn_readfirstlane(p.grid.n_src);
+  gr.N = __builtin_amdgcn_readfirstlane(p.grid.N);
+  gr.len = __builtin_amdgcn_readfirstlane(p.grid.len);
+  asm("" : "+s"(gr.L_src), "+s"(gr.n_src), "+s"(gr.N), "+s"(gr.len));
+  if constexpr (kTabInLds) {
+    // exact tile t: block tab[ns[t]] at tabs[t]; representative row u: tab[u]
+    // at tabs[n_ns + u]
+    for (int i = tid; i < n_ns + n_kv; i += kThreads) tabs[i] = i < n_ns ? tab[ns[i]] : tab[i - n_ns];
+  }
 
   // ---- bitmap of the K_new positions computed exactly ----
   for (int w = tid; w < (n_kv + 31) / 32; w += kThreads) mask[w] = 0u;
@@ -93,8 +114,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
   const int qblk = p.flat[bh * p.n_flat + f];
   // the tail rows of a partial query block read its first row and are not stored
   const int qr = wave * 16 + q;
-  const bool q_ok = qr < p.grid.rows(qblk);
-  const int64_t qrow = (int64_t)p.grid.start(qblk) + (q_ok ? qr : 0);
+  const bool q_ok = qr < gr.rows(qblk);
+  const int64_t qrow = (int64_t)gr.start(qblk) + (q_ok ? qr : 0);
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bf16x8_t qreg[NKK];
 #pragma unroll
@@ -110,33 +131,51 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
 
   // source row r of tile t (exact tiles: rows of K/V; representative tiles:
   // rows of K^c/V^c, past-the-end rows clamped to a valid row and masked later)
-  auto src_row = [&](int t, int r) -> int64_t {
-    if (t < n_ns) {
-      const int blk = tab[ns[t]];  // a partial block repeats its last row
-      return (int64_t)p.grid.start(blk) + min(r, p.grid.rows(blk) - 1);
-    }
-    return tab[min((t - n_ns) * kBN + r, n_kv - 1)];
+  auto exact_blk = [&](int t) -> int {
+    return __builtin_amdgcn_readfirstlane(kTabInLds ? tabs[t] : tab[ns[t]]);
+  };
+  // source row r of representative tile t (rows past n_kv read a valid row
+  // and are masked)
+  auto rep_row = [&](int t, int r) -> int {
+    const int u = min((t - n_ns) * kBN + r, n_kv - 1);
+    return kTabInLds ? tabs[n_ns + u] : tab[u];
   };
   // Partial blocks (the tail of each segment) sit at K_new positions n_src - 1
   // and, if the context tail is kept, n_kv - 1: taken exactly, their missing
   // tokens are masked; as representatives they carry the weight (tokens / b).
-  const int src_tail = p.grid.src_tail();
-  const int ctx_tail = p.grid.ctx_tail();
-  const int pu0 = src_tail ? p.grid.n_src - 1 : -1;
-  const int pu1 = (ctx_tail && tab[n_kv - 1] == p.grid.n_blocks() - 1) ? n_kv - 1 : -1;
-  const float w0 = src_tail ? log2f((float)src_tail / kBN) / p.scale_log2 : 0.0f;
-  const float w1 = ctx_tail ? log2f((float)ctx_tail / kBN) / p.scale_log2 : 0.0f;
+  const int src_tail = gr.src_tail();
+  const int ctx_tail = gr.ctx_tail();
+  const int pu0 = src_tail ? gr.n_src - 1 : -1;
+  const int pu1 = (ctx_tail && tab[n_kv - 1] == gr.n_blocks() - 1) ? n_kv - 1 : -1;
+  float sl2 = p.scale_log2;
+  float exact_bias2 = p.exact_bias_log2;  // -log2(b)
+  asm("" : "+s"(sl2), "+s"(exact_bias2));
+  const float w0 = src_tail ? log2f((float)src_tail / kBN) / sl2 : 0.0f;
+  const float w1 = ctx_tail ? log2f((float)ctx_tail / kBN) / sl2 : 0.0f;
 
   // staging: chunk c = tid + 256 i is row c / KC, 16-byte column c % KC (KC
   // consecutive threads read one row); K and V are both plain row-major copies
   u32x4 st[NCH];
-  auto load_rows = [&](int t, const bf16_bits* full, const bf16_bits* pooled)
+  // blk: the block of exact tile t (read once per tile by the caller)
+  auto load_rows = [&](int t, int blk, const bf16_bits* full, const bf16_bits* pooled)
       __attribute__((always_inline)) {
-    const bf16_bits* b = t < n_ns ? full : pooled;
+    if (t < n_ns) {  // a partial block repeats its last row
+      const int64_t st0 = gr.start(blk);
+      const int last = gr.rows(blk) - 1;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + kThreads * i;
-      st[i] = *reinterpret_cast<const u32x4*>(b + src_row(t, c / KC) * D + (c % KC) * 8);
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + kThreads * i;
+        st[i] = *reinterpret_cast<const u32x4*>(full + (st0 + min(c / KC, last)) * D + (c % KC) * 8);
+      }
+    } else {
+      int rows[NCH];  // pooled row ids (< n_q)
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) rows[i] = rep_row(t, (tid + kThreads * i) / KC);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + kThreads * i;
+        st[i] = *reinterpret_cast<const u32x4*>(pooled + (int64_t)rows[i] * D + (c % KC) * 8);
+      }
     }
   };
   auto store_rows = [&](unsigned char* dst, int stride) __attribute__((always_inline)) {
@@ -154,24 +193,24 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
     for (int i = 0; i < 4; ++i) oacc[j][i] = 0.0f;
   float m_run = -INFINITY;
   float l_run = 0.0f;  // this lane's share of the row sum (reduced at the end)
-  const float sl2 = p.scale_log2;
-  const float exact_bias2 = p.exact_bias_log2;  // -log2(b)
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One K and one V buffer: K(t+1) is loaded while S(t) runs and stored once
   // every wave is past S(t); V(t+1) is loaded while O += V(t) P(t) runs and
   // stored once every wave is past it.  Each store is published by the next
   // barrier, before the first read of that buffer.
-  load_rows(0, Kh, Kch);
+  int blk_cur = n_ns > 0 ? exact_blk(0) : 0;  // block of exact tile t
+  load_rows(0, blk_cur, Kh, Kch);
   store_rows(ks_lds, S::kKStride);
-  load_rows(0, Vh, Vch);
+  load_rows(0, blk_cur, Vh, Vch);
   store_rows(vs_lds, S::kVStride);
   __syncthreads();  // also publishes the bitmap
 
   for (int t = 0; t < n_tiles; ++t) {
     const bool more = t + 1 < n_tiles;
     const bool exact = t < n_ns;
-    if (more) load_rows(t + 1, Kh, Kch);
+    const int blk_nxt = t + 1 < n_ns ? exact_blk(t + 1) : 0;  // block of exact tile t + 1
+    if (more) load_rows(t + 1, blk_nxt, Kh, Kch);
 
     // S^T subtile s: keys 16 s + 4 g + i of query q
     f32x4_t sacc[4];
@@ -190,6 +229,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
     // weight a partial block's row; exact tiles: mask a partial block's tail
     if (!exact) {
       const int u0 = (t - n_ns) * kBN;
+      // bits of keys u0 .. u0 + 63 of the bitmap (u0 is a multiple of 64)
+      const int w0i = u0 >> 5;
+      const uint32_t mlo = mask[w0i];
+      const uint32_t mhi = w0i + 1 < kMaxBlocksPerHead / 32 ? mask[w0i + 1] : 0u;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
@@ -197,11 +240,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
           const int u = u0 + 16 * s4 + 4 * g + i;
           if (u == pu0) sacc[s4][i] += w0;
           if (u == pu1) sacc[s4][i] += w1;
-          if (u >= n_kv || ((mask[u >> 5] >> (u & 31)) & 1u)) sacc[s4][i] = -INFINITY;
+          const int k = 16 * s4 + 4 * g + i;  // key within the tile
+          if (u >= n_kv || (((k < 32 ? mlo : mhi) >> (k & 31)) & 1u)) sacc[s4][i] = -INFINITY;
         }
     } else {
-      const int pos = ns[t];
-      const int vt = (pos == pu0) ? src_tail : ((pos == pu1) ? ctx_tail : kBN);
+      // valid tokens of the block (only the segment tails are partial)
+      const int vt = gr.rows(blk_cur);
       if (vt < kBN) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
@@ -260,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
     __syncthreads();  // every wave is past S(t): K may be overwritten
     if (more) {
       store_rows(ks_lds, S::kKStride);
-      load_rows(t + 1, Vh, Vch);
+      load_rows(t + 1, blk_nxt, Vh, Vch);
     }
     // O^T subtile j (dims 16 j + 4 g + i of query q) += V^T P^T; the V^T operand
     // of chunk c is two transposing reads: keys 32 c + 4 g + (0..3) and
@@ -282,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
     }
     __syncthreads();  // every wave is past O += V(t) P(t); K(t+1) is visible
     if (more) store_rows(vs_lds, S::kVStride);
+    blk_cur = blk_nxt;
   }
 
   // ---- epilogue: O / l, bf16 round-to-nearest-even, LSE (+ ln b) ----
@@ -425,10 +470,18 @@ hipError_t launch_attention_flat(const FlatParams& p, isa_dtype_t dtype, hipStre
   if (dtype == ISA_DTYPE_BF16) {
     const int64_t total = (int64_t)p.n_flat * p.BH;
     const dim3 grid1((unsigned)(((total + 7) / 8) * 8));
-    if (p.D == 128)
-      hipLaunchKernelGGL(attn_flat_bf16_kernel<128>, grid1, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL(attn_flat_bf16_kernel<64>, grid1, dim3(kThreads), 0, stream, p);
+    const bool lds_tab = p.n_ns + p.n_kv <= kLdsTab;
+    if (p.D == 128) {
+      if (lds_tab)
+        hipLaunchKernelGGL((attn_flat_bf16_kernel<128, true>), grid1, dim3(kThreads), 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_flat_bf16_kernel<128, false>), grid1, dim3(kThreads), 0, stream, p);
+    } else {
+      if (lds_tab)
+        hipLaunchKernelGGL((attn_flat_bf16_kernel<64, true>), grid1, dim3(kThreads), 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_flat_bf16_kernel<64, false>), grid1, dim3(kThreads), 0, stream, p);
+    }
   } else {
     if (p.D == 128)
       hipLaunchKernelGGL(attn_flat_f32_kernel<128>, grid, dim3(kF32Threads), 0, stream, p);
