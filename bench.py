@@ -325,7 +325,7 @@ def bench_rope(args, isa, torch, q, k, v, c):
     return {"rope_base": args.rope_base, "latency_ms": ms,
             "dense_equiv_tflops": 4.0 * B * H * N * N * D / (ms * 1e-3) / 1e12,
             "stages_ms": stage_ms,
-            "pool_rope": {"kernel": "pool_kernel<unsigned short, 128, true>", "ms": p_ms,
+            "pool_rope": {"kernel": "pool_kernel<unsigned short, 128, 1>", "ms": p_ms,
                           "algorithmic_bytes": pool_bytes,
                           "GB/s": pool_bytes / (p_ms * 1e-3) / 1e9,
                           "hbm_frac": pool_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
@@ -367,7 +367,7 @@ def bench_block_mask(args, isa, torch, q, k, v, c):
     return {"alpha_ns": args.mask_alpha_ns, "n_ns": info["n_ns"], "latency_ms": ms,
             "dense_equiv_tflops": 4.0 * B * H * N * N * D / (ms * 1e-3) / 1e12,
             "stages_ms": stage_ms,
-            "flat_path": {"kernel": "attn_flat_bf16_kernel<128>", "ms": fl_ms,
+            "flat_path": {"kernel": "attn_flat_bf16_kernel<128, true>", "ms": fl_ms,
                           "algorithmic_tflop": flat_flops / 1e12,
                           "TFLOP/s": flat_flops / (fl_ms * 1e-3) / 1e12,
                           "mfma_frac": flat_flops / (fl_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
