@@ -29,7 +29,7 @@ _DTYPES = {torch.bfloat16: ISA_DTYPE_BF16, torch.float32: ISA_DTYPE_FP32}
 # Every symbol include/isa.h declares.
 EXPORTS = ("isa_plan_create", "isa_plan_get_info", "isa_plan_destroy", "isa_forward",
            "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward", "isa_backward_workspace_bytes",
-           "isa_status_string", "isa_last_hip_error")
+           "isa_status_string", "isa_last_hip_error", "isa_debug_set_flags")
 
 
 class IsaError(RuntimeError):
@@ -87,8 +87,10 @@ def _lib():
         L.isa_status_string.argtypes = [ctypes.c_int]
         L.isa_status_string.restype = ctypes.c_char_p
         L.isa_last_hip_error.argtypes = []
+        L.isa_debug_set_flags.argtypes = [ctypes.c_uint32]
         for name in ("isa_plan_create", "isa_plan_get_info", "isa_plan_destroy", "isa_forward",
-                     "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward", "isa_last_hip_error"):
+                     "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward",
+                     "isa_last_hip_error", "isa_debug_set_flags"):
             getattr(L, name).restype = ctypes.c_int
         _L = L
     return _L
@@ -100,6 +102,14 @@ def isa_status_string(status):
 
 def isa_last_hip_error():
     return int(_lib().isa_last_hip_error())
+
+
+ISA_DEBUG_GLOBAL_TABLES = 1
+
+
+def isa_debug_set_flags(flags):
+    """Diagnostic switches (include/isa.h isa_debug_set_flags); raises on unknown bits."""
+    _check(_lib().isa_debug_set_flags(int(flags)), "isa_debug_set_flags")
 
 
 def _check(status, what):

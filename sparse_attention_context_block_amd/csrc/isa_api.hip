@@ -4,10 +4,17 @@
 // order Taylor paths, merge).  Host code only; every step of the path runs in
 // the device kernels of the other files.
 #include <math.h>
+#include <atomic>
 #include <new>
 #include <string.h>
 
+#include "isa_debug.h"
 #include "isa_internal.h"
+
+namespace isa {
+std::atomic<uint32_t> g_debug_flags{0};
+uint32_t debug_flags() { return g_debug_flags.load(std::memory_order_relaxed); }
+}  // namespace isa
 
 using namespace isa;
 
@@ -88,6 +95,12 @@ const char* isa_status_string(isa_status_t s) {
 }
 
 int isa_last_hip_error(void) { return g_last_hip_error; }
+
+isa_status_t isa_debug_set_flags(uint32_t flags) {
+  if (flags & ~(uint32_t)ISA_DEBUG_GLOBAL_TABLES) return ISA_ERR_INVALID_ARG;
+  isa::g_debug_flags.store(flags, std::memory_order_relaxed);
+  return ISA_OK;
+}
 
 isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   if (!out || !desc) return ISA_ERR_INVALID_ARG;

@@ -28,6 +28,7 @@
 //   every tile (exact: the same max is used in numerator and denominator).
 //   Query blocks of a head are mapped to one XCD so its keys stay in that
 //   XCD's L2.
+#include "isa_debug.h"
 #include "isa_internal.h"
 
 namespace isa {
@@ -372,7 +373,8 @@ hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(((total + 7) / 8) * 8));
   const bool row_table = p.kv_row_table != 0;
   if (!row_table && p.kv_rows % 32 != 0) return hipErrorInvalidValue;
-  const int src = !row_table ? 0 : (p.kv_rows <= kTabLds ? 2 : 1);
+  const bool lds_tab = p.kv_rows <= kTabLds && !(debug_flags() & kDebugGlobalTables);
+  const int src = !row_table ? 0 : (lds_tab ? 2 : 1);
 #define ISA_BF16_LAUNCH(DD, SRC) \
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, SRC>), grid, dim3(kThreads), 0, stream, p)
   if (p.D == 128) {

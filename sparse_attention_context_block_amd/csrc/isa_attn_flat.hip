@@ -26,6 +26,7 @@
 // the S^T accumulators leave in the lane, so P needs no shuffle.  V stays
 // row-major in LDS (a plain copy) and the matching V^T operand comes from two
 // transposing reads (ds_read_b64_tr_b16) per chunk.
+#include "isa_debug.h"
 #include "isa_internal.h"
 
 namespace isa {
@@ -470,7 +471,7 @@ hipError_t launch_attention_flat(const FlatParams& p, isa_dtype_t dtype, hipStre
   if (dtype == ISA_DTYPE_BF16) {
     const int64_t total = (int64_t)p.n_flat * p.BH;
     const dim3 grid1((unsigned)(((total + 7) / 8) * 8));
-    const bool lds_tab = p.n_ns + p.n_kv <= kLdsTab;
+    const bool lds_tab = p.n_ns + p.n_kv <= kLdsTab && !(debug_flags() & kDebugGlobalTables);
     if (p.D == 128) {
       if (lds_tab)
         hipLaunchKernelGGL((attn_flat_bf16_kernel<128, true>), grid1, dim3(kThreads), 0, stream, p);

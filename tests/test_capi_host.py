@@ -31,6 +31,16 @@ def test_library_exports_every_declared_symbol():
     assert sorted(isa.EXPORTS) == declared
 
 
+def test_debug_flags_accept_known_bits_only():
+    # host-only setter: no HIP call
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_GLOBAL_TABLES)
+    isa.isa_debug_set_flags(0)
+    with pytest.raises(RuntimeError, match="INVALID_ARG"):
+        isa.isa_debug_set_flags(2)
+    assert isa._lib().isa_debug_set_flags(0x80000000) == 1  # ISA_ERR_INVALID_ARG
+    isa.isa_debug_set_flags(0)
+
+
 def test_status_strings():
     for s in range(5):
         assert isa.isa_status_string(s).startswith("ISA_")
