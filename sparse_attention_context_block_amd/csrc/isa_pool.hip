@@ -137,11 +137,11 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
       for (int e = 0; e < EPC; ++e) acc[t][e] = 0.0;
 
     const int64_t base = (bh * N + start) * (int64_t)D + c * EPC;
-    auto row = [&](int r, int j) __attribute__((always_inline)) {
+    // rotate (if asked), store the rotated Q and K rows, and add the row's three
+    // chunks to the running sums
+    auto process = [&](int r, int j, const uint4& uq, const uint4& uk, const uint4& uv)
+        __attribute__((always_inline)) {
       const int64_t off = base + (int64_t)r * D;
-      const uint4 uq = *reinterpret_cast<const uint4*>(Q + off);
-      const uint4 uk = *reinterpret_cast<const uint4*>(K + off);
-      const uint4 uv = *reinterpret_cast<const uint4*>(V + off);
       double x[EPC], y[EPC];
       Elt<T>::unpack(uq, x);
       Elt<T>::unpack(uk, y);
@@ -171,13 +171,30 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[2][e] += x[e];
     };
+    auto load = [&](int r, uint4& uq, uint4& uk, uint4& uv) __attribute__((always_inline)) {
+      const int64_t off = base + (int64_t)r * D;
+      uq = *reinterpret_cast<const uint4*>(Q + off);
+      uk = *reinterpret_cast<const uint4*>(K + off);
+      uv = *reinterpret_cast<const uint4*>(V + off);
+    };
     if constexpr (kCache) {
-      // the launcher guarantees block <= kBlock, so JMAX passes cover a block
+      // the launcher guarantees block <= kBlock, so JMAX passes cover a block;
+      // all of this head's loads are issued before the first row is processed
+      // (unconditionally: rows past a partial block's end read its last row and
+      // are not processed; a conditional load makes the wait-count pass hold
+      // each group of loads until the previous group has arrived)
+      uint4 uq[JMAX], uk[JMAX], uv[JMAX];
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j) load(min(r0 + RP * j, rows - 1), uq[j], uk[j], uv[j]);
 #pragma unroll
       for (int j = 0; j < JMAX; ++j)
-        if (r0 + RP * j < rows) row(r0 + RP * j, j);
+        if (r0 + RP * j < rows) process(r0 + RP * j, j, uq[j], uk[j], uv[j]);
     } else {
-      for (int r = r0; r < rows; r += RP) row(r, 0);
+      for (int r = r0; r < rows; r += RP) {
+        uint4 uq, uk, uv;
+        load(r, uq, uk, uv);
+        process(r, 0, uq, uk, uv);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 3; ++t)
