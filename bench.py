@@ -472,8 +472,9 @@ def main():
         return
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (ISA is independent per head; see the sharding "
-              f"note in DESIGN.md); --gpus {args.gpus} is not supported", file=sys.stderr)
+        print(f"bench.py measures one GPU only: every step of ISA is independent per (batch, "
+              f"head), so N GPUs would each run H/N heads with no communication; --gpus "
+              f"{args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         sweep(args)
