@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--rope-steps", type=int, default=10)
     ap.add_argument("--block-lengths", type=int, nargs="*", default=[32, 128],
                     help="also time the forward with these block lengths (none: skip)")
+    ap.add_argument("--gather-steps", type=int, default=10,
+                    help="single calls of the materialised gather to time (0 = skip)")
     ap.add_argument("--dist-reps", type=int, default=30,
                     help="per-call latency percentiles and cold-cache stage times over this "
                          "many single calls (0 = skip)")
@@ -169,6 +171,25 @@ def bench_distribution(args, isa, torch, plan, q, k, v, o, lse, ws, dev, with_de
     _log(f"per-call ISA warm {out['isa_warm_ms']}, cold {out['isa_cold_ms']}")
     _log(f"stages cold {stage['cold']}")
     return out
+
+
+def bench_gather(args, isa, torch, plan, q, k, v):
+    """The materialised gather + concat (isa_gather): K_new, V_new written from
+    the selection of a forward on the same input.  The forward itself fuses
+    the gather into the exact kernel's tile loads and never runs this."""
+    _, _, aux = isa.isa_forward(plan, q, k, v, aux=True)
+    sel = aux["sel"]
+    k_new, v_new = isa.isa_gather(plan, k, v, sel)
+    for _ in range(2):
+        isa.isa_gather(plan, k, v, sel, k_new=k_new, v_new=v_new)
+    ms_list = per_call_ms(torch, lambda: isa.isa_gather(plan, k, v, sel, k_new=k_new,
+                                                        v_new=v_new), args.gather_steps)
+    ms = float(np.median(ms_list))
+    nbytes = 4 * k_new.numel() * k_new.element_size()  # K and V rows, each read and written
+    _log(f"gather {ms:.3f} ms ({nbytes / (ms * 1e-3) / 1e9:.0f} GB/s)")
+    return {"kernel": "gather_kernel", "median_ms": ms, "bytes": int(nbytes),
+            "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def kernel_source_sha256():
@@ -558,6 +579,9 @@ def main():
         _log(f"dense {dms:.3f} ms")
         del od, lsed
 
+    gather = None
+    if args.gather_steps > 0:
+        gather = bench_gather(args, isa, torch, plan, q, k, v)
     dist = None
     if args.dist_reps > 0:
         dist = bench_distribution(args, isa, torch, plan, q, k, v, o, lse, ws, dev,
@@ -605,6 +629,7 @@ def main():
         "dense_baseline": dense,
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
         "latency_distribution": dist,
+        "gather_materialised": gather,
         "roofline": roofline,
         "block_mask": block_mask,
         "rope": rope,

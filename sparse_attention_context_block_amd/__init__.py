@@ -219,15 +219,21 @@ def isa_forward(plan, q, k, v, o=None, lse=None, aux=False, workspace=None, stre
     return o, lse, out_aux
 
 
-def isa_gather(plan, k, v, sel, stream=None):
-    """Materialise K_new, V_new [B, H, l_new, D] from sel [B, H, k]."""
+def isa_gather(plan, k, v, sel, k_new=None, v_new=None, stream=None):
+    """Materialise K_new, V_new [B, H, l_new, D] from sel [B, H, k] (into k_new,
+    v_new if given)."""
     d, info = plan.desc, plan.info
     shape = (d.B, d.H, d.L_src + d.L_ctx, d.D)
     dt = _torch_dtype(plan)
     kp, vp = _dev(k, dt, shape, "k"), _dev(v, dt, shape, "v")
     sp = _dev(sel, torch.int32, (d.B, d.H, info["k"]), "sel") if info["k"] else None
-    k_new = torch.empty((d.B, d.H, info["l_new"], d.D), dtype=dt, device=k.device)
-    v_new = torch.empty_like(k_new)
+    new_shape = (d.B, d.H, info["l_new"], d.D)
+    if k_new is None:
+        k_new = torch.empty(new_shape, dtype=dt, device=k.device)
+    if v_new is None:
+        v_new = torch.empty_like(k_new)
+    _dev(k_new, dt, new_shape, "k_new")
+    _dev(v_new, dt, new_shape, "v_new")
     _check(_lib().isa_gather(plan.handle, kp, vp, sp, k_new.data_ptr(), v_new.data_ptr(),
                              _stream(stream)), "isa_gather")
     return k_new, v_new
