@@ -208,15 +208,22 @@ const char* isa_status_string(isa_status_t status);
 /* The hipError_t of the last failed HIP call on this thread (0 if none). */
 int isa_last_hip_error(void);
 
-/* Diagnostics, for tests of kernel paths that the shapes of small test cases do
- * not reach.  ISA_DEBUG_GLOBAL_TABLES makes the block-mask (flat) and Taylor
- * kernels read their block and row tables from global memory, the path they
- * otherwise take only when a table is too long for its LDS copy (more than 896
- * entries for the block mask, 2048 rows for the Taylor path).  Results are the
- * same either way.  The flags are process-wide and apply to launches issued
- * after the call; set them while no other thread issues launches.  Returns
- * ISA_ERR_INVALID_ARG (and changes nothing) for unknown bits. */
+/* Diagnostics, for tests of kernel paths that the default dispatch or the
+ * shapes of small test cases do not reach.
+ * - ISA_DEBUG_GLOBAL_TABLES makes the block-mask (flat) and Taylor kernels read
+ *   their block and row tables from global memory, the path they otherwise take
+ *   only when a table is too long for its LDS copy (more than 896 entries for
+ *   the block mask, 2048 rows for the Taylor path).  Results are the same
+ *   either way.
+ * - ISA_DEBUG_4WAVE_EXACT runs the bf16 launches that read whole blocks through
+ *   a block table (the exact path, the dense baseline) on the 4-wave kernel
+ *   that otherwise serves only the Taylor path, instead of the ping-pong kernel
+ *   (a slower alternative with the same arithmetic per row, for comparison).
+ * The flags are process-wide and apply to launches issued after the call; set
+ * them while no other thread issues launches.  Returns ISA_ERR_INVALID_ARG (and
+ * changes nothing) for unknown bits. */
 #define ISA_DEBUG_GLOBAL_TABLES 1u
+#define ISA_DEBUG_4WAVE_EXACT 2u
 isa_status_t isa_debug_set_flags(uint32_t flags);
 
 #ifdef __cplusplus

@@ -105,6 +105,7 @@ def isa_last_hip_error():
 
 
 ISA_DEBUG_GLOBAL_TABLES = 1
+ISA_DEBUG_4WAVE_EXACT = 2
 
 
 def isa_debug_set_flags(flags):

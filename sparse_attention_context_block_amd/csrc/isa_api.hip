@@ -97,7 +97,10 @@ const char* isa_status_string(isa_status_t s) {
 int isa_last_hip_error(void) { return g_last_hip_error; }
 
 isa_status_t isa_debug_set_flags(uint32_t flags) {
-  if (flags & ~(uint32_t)ISA_DEBUG_GLOBAL_TABLES) return ISA_ERR_INVALID_ARG;
+  static_assert(isa::kDebugGlobalTables == ISA_DEBUG_GLOBAL_TABLES &&
+                    isa::kDebug4WaveExact == ISA_DEBUG_4WAVE_EXACT,
+                "debug flag bits");
+  if (flags & ~isa::kDebugAll) return ISA_ERR_INVALID_ARG;
   isa::g_debug_flags.store(flags, std::memory_order_relaxed);
   return ISA_OK;
 }

@@ -5,8 +5,7 @@
 //
 // Workgroup = one 64-row query block; 4 threads per query row, each owning a
 // quarter of D.  Keys stream through LDS in 32-row tiles.
-#include <stdlib.h>
-
+#include "isa_debug.h"
 #include "isa_internal.h"
 
 namespace isa {
@@ -105,21 +104,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
   if (p.lse && part == 0) p.lse[bh * p.lse_head_stride + qrow] = m + logf(l) + p.lse_offset;
 }
 
-// ISA_ATTN_4WAVE=1 selects the 4-wave kernel for every bf16 launch (comparison)
-bool force_4wave() {
-  static const bool f = [] {
-    const char* e = getenv("ISA_ATTN_4WAVE");
-    return e && e[0] == '1';
-  }();
-  return f;
-}
-
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream) {
   if (dtype == ISA_DTYPE_BF16) {
     // block tables (exact path, dense): the ping-pong kernel
-    if (!p.kv_row_table && !force_4wave()) return launch_attention_pp(p, stream);
+    if (!p.kv_row_table && !(debug_flags() & kDebug4WaveExact)) return launch_attention_pp(p, stream);
     return launch_attention_bf16(p, stream);
   }
   if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;

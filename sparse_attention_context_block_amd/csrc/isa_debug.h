@@ -9,4 +9,8 @@ uint32_t debug_flags();
 // Matches ISA_DEBUG_GLOBAL_TABLES: the block-mask and Taylor kernels read
 // their tables from global memory even where the copy in LDS would fit.
 constexpr uint32_t kDebugGlobalTables = 1u;
+// Matches ISA_DEBUG_4WAVE_EXACT: block-table launches of the bf16 attention
+// (exact path, dense baseline) run on the 4-wave kernel.
+constexpr uint32_t kDebug4WaveExact = 2u;
+constexpr uint32_t kDebugAll = kDebugGlobalTables | kDebug4WaveExact;
 }  // namespace isa

@@ -34,9 +34,11 @@ def test_library_exports_every_declared_symbol():
 def test_debug_flags_accept_known_bits_only():
     # host-only setter: no HIP call
     isa.isa_debug_set_flags(isa.ISA_DEBUG_GLOBAL_TABLES)
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_4WAVE_EXACT)
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_GLOBAL_TABLES | isa.ISA_DEBUG_4WAVE_EXACT)
     isa.isa_debug_set_flags(0)
     with pytest.raises(RuntimeError, match="INVALID_ARG"):
-        isa.isa_debug_set_flags(2)
+        isa.isa_debug_set_flags(4)
     assert isa._lib().isa_debug_set_flags(0x80000000) == 1  # ISA_ERR_INVALID_ARG
     isa.isa_debug_set_flags(0)
 

@@ -1,6 +1,7 @@
-"""GPU checks of the global-memory table paths of the block-mask (flat) and
-Taylor kernels, through the C ABI.
+"""GPU checks of the kernel paths that only the diagnostic switches of
+isa_debug_set_flags reach, through the C ABI.
 
+Global-memory table paths of the block-mask (flat) and Taylor kernels:
 Both kernels copy their block and row tables into LDS when the tables are
 short enough (every shape a parity test can afford) and read them from global
 memory otherwise.  isa_debug_set_flags(ISA_DEBUG_GLOBAL_TABLES) forces the
@@ -8,8 +9,15 @@ global path: the tables hold the same indices either way, so the outputs and
 the LSE must equal those of the default path bit for bit; one case is also
 checked against the fp64 oracle.  Partial blocks (segment tails) are included
 because the exact tiles of the block mask read their valid-token count from the
-block grid on both paths.  Every case prints its name, shape and seed (flushed)
-before touching the GPU.
+block grid on both paths.
+
+The 4-wave kernel on block tables (ISA_DEBUG_4WAVE_EXACT): by default the
+exact path and the dense baseline run on the ping-pong kernel and the 4-wave
+kernel reads only pooled rows through a row table; with the switch it reads
+whole blocks through the block table instead.  Those cases are checked against
+the fp64 oracle, at every block length and with partial blocks.
+
+Every case prints its name, shape and seed (flushed) before touching the GPU.
 """
 
 import sys
@@ -17,10 +25,12 @@ import sys
 import pytest
 import torch
 
+import oracle as orc
 import sparse_attention_context_block_amd as isa
-from synth import generate
-from tests.parity import to_gpu
+from synth import generate, to_f64
+from tests.parity import check_close, out_f64, to_gpu
 from tests.test_isa_ns_gpu import _parity
+from tests.test_isa_blocks_gpu import _parity as _block_parity
 from tests.parity import BF16_MAX_ABS, BF16_MEAN_ABS
 
 pytestmark = pytest.mark.gpu
@@ -71,3 +81,41 @@ def test_global_tables_block_mask_oracle_parity():
                 (BF16_MAX_ABS, BF16_MEAN_ABS))
     finally:
         isa.isa_debug_set_flags(0)
+
+
+@pytest.mark.parametrize("b,L_src,L_ctx,D,a_s,a_f,seed", [
+    (64, 1024, 1024, 128, 0.25, 0.5, 311),   # aligned
+    (64, 1000, 700, 64, 0.5, 0.25, 312),     # tails 40 and 60, D = 64
+    (32, 500, 300, 128, 0.5, 0.5, 313),      # tails 20 and 12
+    (128, 1000, 700, 128, 0.5, 0.0, 314),    # tails 104 and 60, every query exact
+])
+def test_4wave_exact_path_matches_oracle(b, L_src, L_ctx, D, a_s, a_f, seed):
+    _say(f"4-wave exact B1 H2 L_src{L_src} L_ctx{L_ctx} D{D} b{b} as{a_s} af{a_f} seed{seed}")
+    inp = generate(1, 2, L_src, L_ctx, D, b, seed=seed, variant="icl")
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_4WAVE_EXACT)
+    try:
+        _block_parity(inp, "bf16", 1, 2, L_src, L_ctx, D, b, a_s, a_f)
+    finally:
+        isa.isa_debug_set_flags(0)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_4wave_dense_matches_oracle(D):
+    N, seed = 1536, 315 + D
+    _say(f"4-wave dense bf16 B1 H2 N{N} D{D} seed{seed}")
+    inp = generate(1, 2, N // 2, N // 2, D, 64, seed=seed, variant="plain")
+    q, k, v = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v"))
+    od, ld = isa.isa_dense_forward(q, k, v)
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_4WAVE_EXACT)
+    try:
+        o4, l4 = isa.isa_dense_forward(q, k, v)
+    finally:
+        isa.isa_debug_set_flags(0)
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.dense_ref(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v")))
+    mx, mn = check_close(out_f64(o4), O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (4-wave)")
+    check_close(l4.cpu().numpy(), L_ref, 5e-3, 1e-3, "LSE (4-wave)")
+    # same keys in the same tile order and the same per-row arithmetic as the
+    # ping-pong kernel: identical bits
+    assert torch.equal(o4, od) and torch.equal(l4, ld)
+    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}; equal to the ping-pong kernel")
