@@ -12,6 +12,14 @@ against the oracle: every decision, and sampled output rows.  At this length
 the Taylor path's row table (2560 entries) and the block mask's tables exceed
 their LDS copies, so those kernels read them from global memory.
 
+The backward at the same shape cannot be compared with the oracle (its dK, dV
+need every query row), so besides the head-by-head identity it is checked
+against properties that hold at any size: finite gradients, exact zeros on the
+context rows of unselected blocks, sum_t dV_t = sum_r dO_r (every exact
+row's P and every flat row's pi sum to one, and the Taylor broadcast gives each
+token of block j the share dV^c_j / w_j, so each query row passes its dO on
+whole) and sum_t dK_t = 0 (each row of dS = P (dP - delta) sums to zero).
+
 Every case prints its name, shape and seed (flushed) before touching the GPU.
 """
 
@@ -43,8 +51,8 @@ def _say(msg):
 
 @pytest.fixture(scope="module")
 def drawn():
-    # the first two heads of the [5, 13] draw, as bf16 bits [1, 2, N, D]
-    return generate(B, H, L, L, D, 64, seed=SEED, variant="icl", heads=[0, 1])
+    # the first two heads of the [5, 13] draw, as bf16 bits [1, 2, N, D], with dO
+    return generate(B, H, L, L, D, 64, seed=SEED, variant="icl", heads=[0, 1], grad=True)
 
 
 @pytest.fixture(scope="module")
@@ -52,7 +60,7 @@ def tiled(drawn):
     _say(f"limits: tiling 2 drawn heads to B{B} H{H} N{2 * L} D{D} on cuda:0")
     idx = torch.arange(B * H, device="cuda") % 2
     out = {}
-    for x in ("q", "k", "v"):
+    for x in ("q", "k", "v", "do"):
         base = to_gpu(drawn[x], "bf16")[0]                # [2, N, D]
         out[x] = base.index_select(0, idx).reshape(B, H, 2 * L, D)
         del base
@@ -148,3 +156,40 @@ def test_limit_longest_sequence_b128():
     check_close(lse.cpu().numpy()[0, 0, rows], L_ref[0, 0], 5e-3, 1e-3, "LSE")
     assert torch.isfinite(o).all()
     _say(f"ok exemptions sel/route {ex}")
+
+
+def test_limit_backward_65_heads(drawn, tiled):
+    N = 2 * L
+    _say(f"limits backward bf16 B{B} H{H} N{N} D{D} as{A_S} af{A_F} seed {SEED} "
+         f"(heads repeat 2 drawn heads)")
+    plan = isa.isa_plan_create(B, H, L, L, D, 64, A_S, A_F)
+    o, lse, aux = isa.isa_forward(plan, tiled["q"], tiled["k"], tiled["v"], aux=True)
+    grads = isa.isa_backward(plan, tiled["q"], tiled["k"], tiled["v"], o, tiled["do"], lse, aux)
+    torch.cuda.synchronize()
+    del o, lse
+    _say("limits: backward done; comparing every head with its drawn head")
+    for name, g in zip(("dQ", "dK", "dV"), grads):
+        gf = g.view(B * H, N, D).view(torch.int16)
+        for i in range(2, B * H):
+            assert torch.equal(gf[i], gf[i % 2]), f"{name} of head {i} differs from head {i % 2}"
+        assert torch.isfinite(g).all(), name
+    sel = aux["sel"].cpu().numpy().reshape(B * H, -1)
+    dk, dv = (out_f64(g[0, :2]) for g in grads[1:])
+    n_src, n_ctx = L // 64, L // 64
+    for h in range(2):
+        # unselected context blocks: exact zeros
+        dropped = np.setdiff1d(np.arange(n_ctx), sel[h])
+        rows = (L + 64 * dropped[:, None] + np.arange(64)[None, :]).ravel()
+        assert not dk[h, rows].any() and not dv[h, rows].any(), f"head {h}: unselected rows"
+        # every query row passes its dO on whole: sum_t dV_t = sum_r dO_r, to
+        # the rounding of the bf16 P, pi and dV (random signs: compared with
+        # the root sum of squares of the terms)
+        do = _drawn_head(drawn["do"], h)[0, 0]
+        lhs, rhs = dv[h].sum(axis=0), do.sum(axis=0)
+        scale = np.sqrt((dv[h] ** 2).sum(axis=0) + (do ** 2).sum(axis=0))
+        err = np.abs(lhs - rhs) / scale
+        assert err.max() <= 0.05, f"head {h}: sum dV vs sum dO, {err.max():.3e} of the RSS"
+        err_k = np.abs(dk[h].sum(axis=0)) / np.sqrt((dk[h] ** 2).sum(axis=0))
+        assert err_k.max() <= 0.05, f"head {h}: sum dK, {err_k.max():.3e} of the RSS"
+        _say(f"head {h}: {len(dropped)} unselected blocks zero; |sum dV - sum dO| / RSS "
+             f"max {err.max():.2e}; |sum dK| / RSS max {err_k.max():.2e}")
