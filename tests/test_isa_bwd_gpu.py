@@ -89,7 +89,7 @@ def test_backward_deterministic():
         assert torch.equal(a, b)
 
 
-def test_backward_workload_b2_n16384_sampled_heads():
+def test_backward_workload_b2_n16384():
     c = CONFIGS[5]
     B, H, L_src, L_ctx, D = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"]
     _say(f"bwd workload {c['name']} seed {c['seed']}")
@@ -103,3 +103,15 @@ def test_backward_workload_b2_n16384_sampled_heads():
         ref = orc.isa_ref_bwd(*(to_f64(inp[x][sl], "bf16") for x in ("q", "k", "v", "do")),
                               L_src, L_ctx, 64, aux["sel"][sl], aux["flat"][sl])
         _check_grads([g[sl] for g in got], ref, f"head ({bi},{h})")
+    # every head: sum_t dV_t = sum_r dO_r and sum_t dK_t = 0 (each P or pi row
+    # sums to one, each dS row to zero, and the Taylor broadcast gives every
+    # token of block j the share dV^c_j / w_j), to the rounding of the bf16
+    # operands and outputs, compared with the root sum of squares of the terms
+    dk, dv = got[1], got[2]
+    do = to_f64(inp["do"], "bf16")
+    err_v = np.abs(dv.sum(axis=2) - do.sum(axis=2)) / np.sqrt((dv ** 2).sum(axis=2)
+                                                              + (do ** 2).sum(axis=2))
+    err_k = np.abs(dk.sum(axis=2)) / np.sqrt((dk ** 2).sum(axis=2))
+    assert err_v.max() <= 0.05 and err_k.max() <= 0.05, (err_v.max(), err_k.max())
+    _say(f"every head: |sum dV - sum dO| / RSS max {err_v.max():.2e}, "
+         f"|sum dK| / RSS max {err_k.max():.2e}")
