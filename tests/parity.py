@@ -136,3 +136,18 @@ def fixed_ref_rows(q, k, v, dtype, L_src, L_ctx, b, sel, flat, rows, heads=None)
         Os.append(O[0, 0])
         Ls.append(L[0, 0])
     return np.stack(Os), np.stack(Ls)
+
+
+def check_in_value_range(o, v):
+    """Each output row is a convex combination of value rows: exact rows weight
+    rows of V, flat rows the block means of V (rounded once to the storage
+    type, so still inside V's range), a masked flat row both.  Every element of
+    O therefore lies between the smallest and the largest value of its head in
+    that dim.  Holds at any size; checked at every row.  o, v: GPU tensors
+    [B, H, N, D]."""
+    lo = v.amin(dim=2, keepdim=True).float()
+    hi = v.amax(dim=2, keepdim=True).float()
+    tol = 1e-6 * torch.maximum(lo.abs(), hi.abs())  # fp32 accumulation
+    of = o.float()
+    bad = int(((of < lo - tol) | (of > hi + tol)).sum().item())
+    assert bad == 0, f"{bad} elements of O outside the value range of their head"

@@ -32,8 +32,8 @@ import torch
 import oracle as orc
 import sparse_attention_context_block_amd as isa
 from synth import generate, to_f64
-from tests.parity import (BF16_MAX_ABS, BF16_MEAN_ABS, check_close, check_ns, check_routing,
-                          check_selection, out_f64, to_gpu)
+from tests.parity import (BF16_MAX_ABS, BF16_MEAN_ABS, check_close, check_in_value_range,
+                          check_ns, check_routing, check_selection, out_f64, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +126,7 @@ def test_limit_4096_blocks_65_heads(drawn, tiled, a_ns):
         check_close(O_gpu[h, rows], O_ref[0, 0], BF16_MAX_ABS, BF16_MEAN_ABS, f"O head {h}")
         check_close(lse_gpu[h, rows], L_ref[0, 0], 5e-3, 1e-3, f"LSE head {h}")
     assert torch.isfinite(o).all()
+    check_in_value_range(o, tiled["v"])
     _say(f"ok exemptions sel/route/mask {ex}")
 
 
@@ -155,6 +156,7 @@ def test_limit_longest_sequence_b128():
     check_close(out_f64(o)[0, 0, rows], O_ref[0, 0], BF16_MAX_ABS, BF16_MEAN_ABS, "O")
     check_close(lse.cpu().numpy()[0, 0, rows], L_ref[0, 0], 5e-3, 1e-3, "LSE")
     assert torch.isfinite(o).all()
+    check_in_value_range(o, v)
     _say(f"ok exemptions sel/route {ex}")
 
 

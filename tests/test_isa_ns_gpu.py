@@ -20,7 +20,8 @@ import oracle as orc
 import sparse_attention_context_block_amd as isa
 from synth import CONFIGS, generate, generate_config, to_f64
 from tests.parity import (BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS, FP32_MEAN_ABS, check_close,
-                          check_ns, check_routing, check_selection, out_f64, to_gpu)
+                          check_in_value_range, check_ns, check_routing, check_selection, out_f64,
+                          to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,4 +148,5 @@ def test_mask_workload_n32768_pages_default():
         check_close(O_gpu[0, h, rows], O_ref[0, 0], BF16_MAX_ABS, BF16_MEAN_ABS, f"O head {h}")
         check_close(lse[0, h, rows], L_ref[0, 0], 5e-3, 1e-3, f"LSE head {h}")
     assert torch.isfinite(o.float()).all()
+    check_in_value_range(o, to_gpu(inp["v"], "bf16"))
     _say(f"ok exemptions sel/route/mask {ex}")

@@ -19,7 +19,8 @@ import oracle as orc
 import sparse_attention_context_block_amd as isa
 from synth import generate, to_f64
 from tests.parity import (BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS, FP32_MEAN_ABS, check_close,
-                          check_routing, check_selection, out_f64, per_head_decisions, to_gpu)
+                          check_in_value_range, check_routing, check_selection, out_f64,
+                          per_head_decisions, to_gpu)
 from tests.test_isa_ns_gpu import _check_all_decisions
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +69,7 @@ def _parity(inp, dtype, B, H, L_src, L_ctx, D, a_s, a_f, a_ns=0.0, rows=None, he
         check_close(got_l, L_ref[0, 0], 5e-3 if dtype == "bf16" else 1e-5,
                     1e-3 if dtype == "bf16" else 1e-6, what=f"LSE head ({bi},{h})")
     assert torch.isfinite(o.float()).all()
+    check_in_value_range(o, to_gpu(inp["v"], dtype))
     _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e} exemptions {ex}")
     return plan, o, aux
 
