@@ -49,15 +49,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload id (synth.CONFIGS)")
+    ap.add_argument("--workload", default="isa_bf16_N32768",
+                    help="workload name (synth.CONFIGS)")
     ap.add_argument("--alpha-s", type=float, default=None)
     ap.add_argument("--alpha-f", type=float, default=None)
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=3,
                     help="heads of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--bwd-config", type=int, default=5,
-                    help="workload of the backward measurement (0: skip)")
+    ap.add_argument("--bwd-workload", default="isa_fwd_bwd_bf16_B2_N16384",
+                    help="workload of the backward measurement (none: skip)")
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--mask-alpha-ns", type=float, default=0.0625,
                     help="also time the forward with this block-mask ratio (0 = skip)")
@@ -259,11 +260,11 @@ def bench_backward(args, isa, torch, dev):
     """Forward + decision-frozen backward on the backward workload."""
     from synth import CONFIGS, generate_config
 
-    c = CONFIGS[args.bwd_config]
+    c = CONFIGS[args.bwd_workload]
     B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
     N = L_src + L_ctx
     _log(f"backward workload {c['name']}")
-    inp = generate_config(args.bwd_config)
+    inp = generate_config(args.bwd_workload)
     to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v, do = (to_gpu(inp[x]) for x in ("q", "k", "v", "do"))
     del inp
@@ -506,7 +507,7 @@ def main():
     import sparse_attention_context_block_amd as isa
     from synth import CONFIGS, generate_config
 
-    c = dict(CONFIGS[args.config])
+    c = dict(CONFIGS[args.workload])
     if args.alpha_s is not None:
         c["alpha_s"] = args.alpha_s
     if args.alpha_f is not None:
@@ -515,7 +516,7 @@ def main():
     N = L_src + L_ctx
     _log(f"workload {c['name']} B{B} H{H} N{N} D{D} as{c['alpha_s']} af{c['alpha_f']}")
     t0 = time.perf_counter()
-    inp = generate_config(args.config)
+    inp = generate_config(args.workload)
     _log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
 
     dev = torch.device("cuda:0")
@@ -608,7 +609,7 @@ def main():
                         "TFLOP/s": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12},
     }
     backward = None
-    if args.bwd_config:
+    if args.bwd_workload != "none":
         del o, lse, ws
         backward = bench_backward(args, isa, torch, dev)
     cpu = None

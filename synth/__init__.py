@@ -28,19 +28,19 @@ returned as their uint16 bit patterns.
 
 import numpy as np
 
-# The workloads: a tiny fp32 case, then the bf16 cases at the pages' 5K-50K
-# token scale (H = 40 heads of D = 128, blocks of 64 tokens).
+# The workloads, by name: a tiny fp32 case, then the bf16 cases at the pages'
+# 5K-50K token scale (H = 40 heads of D = 128, blocks of 64 tokens).
 CONFIGS = {
-    1: dict(name="tiny_fp32_N512", B=1, H=2, D=64, L_src=256, L_ctx=256, block=64,
+    "tiny_fp32_N512": dict(name="tiny_fp32_N512", B=1, H=2, D=64, L_src=256, L_ctx=256, block=64,
             alpha_s=0.5, alpha_f=0.5, dtype="fp32", variant="tiny", seed=1001),
-    2: dict(name="isa_bf16_N8192", B=1, H=40, D=128, L_src=4096, L_ctx=4096, block=64,
+    "isa_bf16_N8192": dict(name="isa_bf16_N8192", B=1, H=40, D=128, L_src=4096, L_ctx=4096, block=64,
             alpha_s=0.25, alpha_f=0.5, dtype="bf16", variant="icl", seed=1002),
-    3: dict(name="isa_bf16_N32768", B=1, H=40, D=128, L_src=16384, L_ctx=16384, block=64,
+    "isa_bf16_N32768": dict(name="isa_bf16_N32768", B=1, H=40, D=128, L_src=16384, L_ctx=16384, block=64,
             alpha_s=0.25, alpha_f=0.5, dtype="bf16", variant="icl", seed=1003),
-    4: dict(name="isa_bf16_N51200", B=1, H=40, D=128, L_src=25600, L_ctx=25600, block=64,
+    "isa_bf16_N51200": dict(name="isa_bf16_N51200", B=1, H=40, D=128, L_src=25600, L_ctx=25600, block=64,
             alpha_s=0.25, alpha_f=0.5, dtype="bf16", variant="icl", seed=1004,
             sweep_alpha_s=(0.125, 0.25, 0.5), sweep_alpha_f=(0.25, 0.5, 0.75)),
-    5: dict(name="isa_fwd_bwd_bf16_B2_N16384", B=2, H=40, D=128, L_src=8192, L_ctx=8192,
+    "isa_fwd_bwd_bf16_B2_N16384": dict(name="isa_fwd_bwd_bf16_B2_N16384", B=2, H=40, D=128, L_src=8192, L_ctx=8192,
             block=64, alpha_s=0.25, alpha_f=0.5, dtype="bf16", variant="icl", seed=1005,
             grad=True),
 }
@@ -128,9 +128,9 @@ def generate(B, H, L_src, L_ctx, D, block, seed, variant="icl", dtype="bf16",
     return {nm: a.reshape(1, len(keep), N, D) for nm, a in out.items()}
 
 
-def generate_config(cfg_id, heads=None, **overrides):
+def generate_config(name, heads=None, **overrides):
     """Inputs of one of the named workloads (see CONFIGS)."""
-    c = dict(CONFIGS[cfg_id])
+    c = dict(CONFIGS[name])
     c.update(overrides)
     return generate(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"], c["seed"],
                     variant=c["variant"], dtype=c["dtype"], grad=c.get("grad", False),

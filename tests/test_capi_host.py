@@ -50,9 +50,9 @@ def test_status_strings():
     assert isa.isa_last_hip_error() == 0
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_plan_info_matches_oracle_counts(cfg):
-    c = CONFIGS[cfg]
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_plan_info_matches_oracle_counts(name):
+    c = CONFIGS[name]
     dt = "bf16" if c["dtype"] == "bf16" else "fp32"
     import torch
     p = isa.isa_plan_create(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"],

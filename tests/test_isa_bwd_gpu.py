@@ -90,10 +90,10 @@ def test_backward_deterministic():
 
 
 def test_backward_workload_b2_n16384():
-    c = CONFIGS[5]
+    c = CONFIGS["isa_fwd_bwd_bf16_B2_N16384"]
     B, H, L_src, L_ctx, D = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"]
     _say(f"bwd workload {c['name']} seed {c['seed']}")
-    inp = generate_config(5)
+    inp = generate_config("isa_fwd_bwd_bf16_B2_N16384")
     plan, grads, aux = _fwd_bwd(inp, B, H, L_src, L_ctx, D, c["alpha_s"], c["alpha_f"])
     got = [out_f64(g) for g in grads]
     for g in got:

@@ -110,9 +110,9 @@ def test_dense_bf16_long_keys():
 
 # --------------------------------------------------------- ISA, small ------
 def test_isa_tiny_fp32_config():
-    c = CONFIGS[1]
+    c = CONFIGS["tiny_fp32_N512"]
     _say(f"ISA tiny fp32 {c}")
-    inp = generate_config(1)
+    inp = generate_config("tiny_fp32_N512")
     _full_parity(inp, "fp32", c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["alpha_s"],
                  c["alpha_f"], (FP32_MAX_ABS, FP32_MEAN_ABS))
 
@@ -204,15 +204,15 @@ def _sample_rows(N, n, seed):
     return np.unique(np.concatenate([rows, [0, N - 1]]))
 
 
-def _workload_parity(cfg_id, alpha_s=None, alpha_f=None, heads_out=4, rows_out=384, inp=None):
-    c = dict(CONFIGS[cfg_id])
+def _workload_parity(name, alpha_s=None, alpha_f=None, heads_out=4, rows_out=384, inp=None):
+    c = dict(CONFIGS[name])
     if alpha_s is not None:
         c["alpha_s"], c["alpha_f"] = alpha_s, alpha_f
     B, H, L_src, L_ctx, D = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"]
     _say(f"workload {c['name']} B{B} H{H} N{L_src + L_ctx} as{c['alpha_s']} af{c['alpha_f']} "
          f"seed {c['seed']}")
     if inp is None:
-        inp = generate_config(cfg_id)
+        inp = generate_config(name)
     plan, o, lse, aux = _run_isa(inp, "bf16", B, H, L_src, L_ctx, D, c["alpha_s"], c["alpha_f"])
     ref = per_head_decisions(inp["q"], inp["k"], "bf16", L_src, L_ctx, 64, c["alpha_s"],
                              c["alpha_f"])
@@ -238,18 +238,18 @@ def _workload_parity(cfg_id, alpha_s=None, alpha_f=None, heads_out=4, rows_out=3
 
 
 def test_workload_n8192_bf16():
-    _workload_parity(2, heads_out=8, rows_out=512)
+    _workload_parity("isa_bf16_N8192", heads_out=8, rows_out=512)
 
 
 def test_workload_n32768_bf16_headline():
-    _workload_parity(3, heads_out=4, rows_out=384)
+    _workload_parity("isa_bf16_N32768", heads_out=4, rows_out=384)
 
 
 def test_workload_n51200_bf16_sweep():
-    inp = generate_config(4)
+    inp = generate_config("isa_bf16_N51200")
     for a_s, a_f in ((0.125, 0.25), (0.25, 0.5), (0.5, 0.75)):
-        _workload_parity(4, a_s, a_f, heads_out=2, rows_out=256, inp=inp)
+        _workload_parity("isa_bf16_N51200", a_s, a_f, heads_out=2, rows_out=256, inp=inp)
 
 
 def test_workload_b2_n16384_forward():
-    _workload_parity(5, heads_out=4, rows_out=384)
+    _workload_parity("isa_fwd_bwd_bf16_B2_N16384", heads_out=4, rows_out=384)

@@ -90,9 +90,9 @@ def test_mask_bf16_small_full_parity(B, H, L_src, L_ctx, D, a_s, a_f, a_ns, seed
 
 
 def test_mask_fp32_tiny():
-    c = CONFIGS[1]
+    c = CONFIGS["tiny_fp32_N512"]
     _say(f"mask fp32 {c['name']} ans 0.34")
-    inp = generate_config(1)
+    inp = generate_config("tiny_fp32_N512")
     _parity(inp, "fp32", c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["alpha_s"],
             c["alpha_f"], 0.34, (FP32_MAX_ABS, FP32_MEAN_ABS))
 
@@ -127,11 +127,11 @@ def test_mask_changes_only_flat_rows_and_is_deterministic():
 def test_mask_workload_n32768_pages_default():
     # the pages' default no-sparsity ratio at the 32K workload: every decision
     # of every head, sampled output rows of four heads
-    c = CONFIGS[3]
+    c = CONFIGS["isa_bf16_N32768"]
     a_ns = 0.0625
     B, H, L_src, L_ctx, D = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"]
     _say(f"mask workload {c['name']} ans {a_ns} seed {c['seed']}")
-    inp = generate_config(3)
+    inp = generate_config("isa_bf16_N32768")
     plan, o, lse, aux = _run(inp, "bf16", B, H, L_src, L_ctx, D, c["alpha_s"], c["alpha_f"], a_ns)
     assert plan.info["n_ns"] == 20
     ex = _check_all_decisions(inp, "bf16", plan, aux, L_src, L_ctx, c["alpha_s"], c["alpha_f"])
