@@ -7,7 +7,11 @@ context tokens) and rounds them to the storage dtype.
 
 The pages measure on real video latents of a 14B editing model at 5K-50K
 tokens ([notes] "research background"; [summary] 1 Introduction); those are
-not available, and these generators stand in for them.
+not available, and these generators stand in for them.  ([notes]: the
+papernotes.org ICML 2026 notes "Lightning Unified Video Editing via In-Context
+Sparse Attention"; [summary]: the paperlayer.ai summary "LIVEditor-14B:
+Lightning Unified Video Editing via In-Context Sparse Attention" of arXiv
+2605.04569v2.)
 
 Recipe (per (batch, head), in this order, from ``numpy.random.default_rng(seed)``):
   Q, K, V ~ N(0, 1) of shape (N, D), drawn as float32;

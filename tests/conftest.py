@@ -1,3 +1,12 @@
+"""Test configuration.
+
+Tests cite the two pages that describe ISA by title and section:
+[notes] is the papernotes.org ICML 2026 notes "Lightning Unified Video Editing
+via In-Context Sparse Attention"; [summary] is the paperlayer.ai summary
+"LIVEditor-14B: Lightning Unified Video Editing via In-Context Sparse
+Attention" of arXiv 2605.04569v2.
+"""
+
 import os
 import sys
 
