@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--rope-steps", type=int, default=10)
     ap.add_argument("--block-lengths", type=int, nargs="*", default=[32, 128],
                     help="also time the forward with these block lengths (none: skip)")
+    ap.add_argument("--partial-shift", type=int, default=24,
+                    help="also time the input cut with the source this many tokens shorter "
+                         "(both segments end in a partial block; 0 = skip)")
     ap.add_argument("--gather-steps", type=int, default=10,
                     help="single calls of the materialised gather to time (0 = skip)")
     ap.add_argument("--dist-reps", type=int, default=30,
@@ -373,6 +376,39 @@ def bench_block_lengths(args, isa, torch, q, k, v, c):
     return out
 
 
+def bench_partial_blocks(args, isa, torch, q, k, v, c):
+    """The same input cut with the source `partial_shift` tokens shorter and the
+    context as much longer, so both segments end in a partial block: latency,
+    stage times and the exact path's rate.  Its algorithmic flops count the
+    valid rows only (of the sharp query blocks and of K_new), which follow the
+    decisions, so one more forward returns them."""
+    s = args.partial_shift
+    cp = dict(c, L_src=c["L_src"] - s, L_ctx=c["L_ctx"] + s)
+    B, H, L_src, L_ctx, D, b = cp["B"], cp["H"], cp["L_src"], cp["L_ctx"], cp["D"], cp["block"]
+    ms, stage_ms, info = _time_variant(isa, torch, q, k, v, cp, args.mask_steps)
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, cp["alpha_s"], cp["alpha_f"])
+    _, _, aux = isa.isa_forward(plan, q, k, v, aux=True)
+    torch.cuda.synchronize()
+    n_src = info["n_src_blocks"]
+    src_len = np.minimum(b, L_src - b * np.arange(n_src))
+    ctx_len = np.minimum(b, L_ctx - b * np.arange(info["n_ctx_blocks"]))
+    blk_len = np.concatenate([src_len, ctx_len])
+    sharp = aux["sharp"].cpu().numpy().reshape(B * H, -1)
+    sel = aux["sel"].cpu().numpy().reshape(B * H, -1)
+    pairs = sum(int(blk_len[sharp[i]].sum()) * (L_src + int(ctx_len[sel[i]].sum()))
+                for i in range(B * H))
+    ex_flops = 4.0 * D * pairs
+    ex_ms = stage_ms["attn_exact"]
+    _log(f"partial blocks (tails {L_src % b}, {L_ctx % b}): ISA forward {ms:.3f} ms; "
+         f"exact path {ex_ms:.3f} ms")
+    return {"L_src": L_src, "L_ctx": L_ctx, "tails": [L_src % b, L_ctx % b], "latency_ms": ms,
+            "dense_equiv_tflops": 4.0 * B * H * (L_src + L_ctx) ** 2 * D / (ms * 1e-3) / 1e12,
+            "stages_ms": stage_ms,
+            "attn_exact": {"ms": ex_ms, "algorithmic_tflop": ex_flops / 1e12,
+                           "TFLOP/s": ex_flops / (ex_ms * 1e-3) / 1e12,
+                           "mfma_frac": ex_flops / (ex_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+
+
 def bench_block_mask(args, isa, torch, q, k, v, c):
     """The same workload with the block mask inside flat query blocks
     (alpha_ns > 0): latency, stage times and the flat-path kernel's rate."""
@@ -560,6 +596,9 @@ def main():
     block_lengths = None
     if args.block_lengths:
         block_lengths = bench_block_lengths(args, isa, torch, q, k, v, c)
+    partial_blocks = None
+    if args.partial_shift > 0:
+        partial_blocks = bench_partial_blocks(args, isa, torch, q, k, v, c)
 
     dense = None
     if not args.no_dense:
@@ -635,6 +674,7 @@ def main():
         "block_mask": block_mask,
         "rope": rope,
         "block_lengths": block_lengths,
+        "partial_blocks": partial_blocks,
         "backward": backward,
         "cpu_baseline": cpu,
     }
