@@ -38,6 +38,7 @@ EXACT_KERNEL_SRC = tuple(os.path.join(ROOT, "sparse_attention_context_block_amd"
                          for f in ("isa_attn_pp.hip", "isa_internal.h"))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP64_TFLOPS = 78.6     # MI355X dense fp64
 
 
 def _log(msg):
@@ -304,6 +305,12 @@ def bench_backward(args, isa, torch, dev):
             "bwd_tflops": bwd_flops / (bms * 1e-3) / 1e12,
             "bwd_mfma_frac": bwd_flops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12}
+
+
+def _fp64_rate(ms, flops):
+    """Stage time with its fp64 rate against the fp64 peak."""
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "fp64_TFLOP/s": tf, "fp64_frac": tf / PEAK_FP64_TFLOPS}
 
 
 def _time_variant(isa, torch, q, k, v, c, steps, alpha_ns=0.0, rope_base=0.0):
@@ -640,12 +647,18 @@ def main():
     stages = {
         "pool": {"ms": stage_ms["pool"], "GB/s": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9,
                  "hbm_frac": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "coarse_rowstats": {"ms": stage_ms["coarse_rowstats"]},
-        "coarse_colsum": {"ms": stage_ms["coarse_colsum"]},
+        # the coarse logits: 2 D fp64 flops per (query block, key block) for the
+        # row statistics, per (source block, context block) for the column means
+        "coarse_rowstats": _fp64_rate(stage_ms["coarse_rowstats"],
+                                      2.0 * D * B * H * info["n_q_blocks"] ** 2),
+        "coarse_colsum": _fp64_rate(stage_ms["coarse_colsum"],
+                                    2.0 * D * B * H * info["n_src_blocks"] * info["n_ctx_blocks"]),
         "select_route": {"ms": stage_ms["select_route"]},
         "attn_exact": {"ms": ex_ms, "TFLOP/s": achieved, "mfma_frac": achieved / PEAK_BF16_TFLOPS},
         "attn_taylor": {"ms": stage_ms["attn_taylor"],
-                        "TFLOP/s": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12},
+                        "TFLOP/s": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12,
+                        "mfma_frac": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12
+                        / PEAK_BF16_TFLOPS},
     }
     backward = None
     if args.bwd_workload != "none":
