@@ -167,6 +167,8 @@ isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K,
  * [summary] 3 Pre-Selection), materialised: K_new, V_new [B, H, l_new, D] =
  * [all source tokens ; tokens of the context blocks listed in sel, in the
  * order given].  sel: device [B, H, k] int32 (as written by isa_forward).
+ * The ids are read on the device and not checked: each must lie in
+ * [0, n_ctx_blocks), or the copy reads outside K and V.
  * isa_forward itself never materialises K_new: its attention kernels read
  * the same rows through the block table.  Errors: ISA_ERR_INVALID_ARG,
  * ISA_ERR_UNSUPPORTED (L_src or L_ctx not a multiple of the block length: the
@@ -190,7 +192,11 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * no gradient passes through the coarse map.  Context rows that were not
  * selected receive zero.  Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D]; lse:
  * [B, H, N] float from the forward; aux: sel, flat and sharp from the
- * forward (required).  workspace: at least isa_backward_workspace_bytes().
+ * forward (required).  The decisions are read on the device and not checked:
+ * they must be what isa_forward wrote for this plan (sel: k distinct ascending
+ * context block ids; flat and sharp: together every query block once, each
+ * list ascending), or the kernels read and write outside the tensors.
+ * workspace: at least isa_backward_workspace_bytes().
  * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, block != 64, a
  * plan with n_ns > 0 or rope_base > 0, or L_src / L_ctx not a multiple of
  * 64), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
