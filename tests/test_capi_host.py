@@ -258,3 +258,13 @@ def test_python_binding_refuses_cpu_tensors():
         isa.isa_forward(p, x, x, x)
     with pytest.raises(TypeError):
         isa.isa_dense_forward(x, x, x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no CPU fallback: without the HIP library every entry point raises
+    monkeypatch.setattr(isa, "_L", None)
+    monkeypatch.setattr(isa, "LIB_PATH", str(tmp_path / "libisa.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        isa.isa_plan_create(1, 1, 64, 64, 64)
+    with pytest.raises(RuntimeError, match="not built"):
+        isa._lib()
