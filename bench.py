@@ -79,6 +79,12 @@ def parse():
                          "many single calls (0 = skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the workload line: ISA vs dense over N = 5K..64K")
+    ap.add_argument("--sweep-steps", type=int, default=10,
+                    help="timed ISA calls per length of the N sweep (0 = skip the sweep "
+                         "section of the workload line)")
+    ap.add_argument("--c4-steps", type=int, default=10,
+                    help="timed calls per (alpha_s, alpha_f) point of the N=51200 grid "
+                         "(0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, launch a plain 256 MiB fp32 copy kernel (x2 scale) "
                          "whose FETCH_SIZE / WRITE_SIZE calibrate the HBM counters")
@@ -86,29 +92,41 @@ def parse():
 
 
 def cpu_baseline(inp, c, n_heads):
-    """Time the fp64 oracle on the first n_heads heads, extrapolate to the job."""
+    """Time the fp64 oracle (isa_ref, and dense_ref for the dense baseline) on
+    the first n_heads heads of the workload's input; extrapolate each to the job."""
     import threadpoolctl
 
     import oracle as orc
     from synth import to_f64
 
     B, H = c["B"], c["H"]
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    t0 = time.perf_counter()
-    for h in range(n_heads):
-        sl = (slice(0, 1), slice(h, h + 1))
-        orc.isa_ref(to_f64(inp["q"][sl], "bf16"), to_f64(inp["k"][sl], "bf16"),
-                    to_f64(inp["v"][sl], "bf16"), c["L_src"], c["L_ctx"], c["block"],
-                    c["alpha_s"], c["alpha_f"])
-    dt = time.perf_counter() - t0
-    per_job_s = dt / n_heads * (B * H)
+    blas = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
     N = c["L_src"] + c["L_ctx"]
     dense_flops = 4.0 * B * H * N * N * c["D"]
-    return {"value": dense_flops / per_job_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
-            "cores": int(threads), "kind": "oracle",
-            "latency_ms_extrapolated": per_job_s * 1e3,
-            "sample": f"isa_ref (fp64 NumPy) on {n_heads} of {B * H} heads of the same input, "
-                      f"{dt:.1f} s, extrapolated linearly to all heads"}
+    heads = [(slice(0, 1), slice(h, h + 1)) for h in range(n_heads)]
+    args = [tuple(to_f64(inp[x][sl], "bf16") for x in ("q", "k", "v")) for sl in heads]
+    t0 = time.perf_counter()
+    for q64, k64, v64 in args:
+        orc.isa_ref(q64, k64, v64, c["L_src"], c["L_ctx"], c["block"], c["alpha_s"],
+                    c["alpha_f"])
+    t_isa = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for q64, k64, v64 in args:
+        orc.dense_ref(q64, k64, v64)
+    t_dense = time.perf_counter() - t0
+    isa_job_s = t_isa / n_heads * (B * H)
+    dense_job_s = t_dense / n_heads * (B * H)
+    return {"value": dense_flops / isa_job_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+            "cores": int(cores), "blas_threads": int(blas), "kind": "oracle",
+            "latency_ms_extrapolated": isa_job_s * 1e3,
+            "dense_ref": {"latency_ms_extrapolated": dense_job_s * 1e3,
+                          "tflops": dense_flops / dense_job_s / 1e12,
+                          "sample_s": t_dense},
+            "sample": f"isa_ref and dense_ref (fp64 NumPy) each on heads 0-{n_heads - 1} of "
+                      f"{B * H} of the same input ({t_isa:.1f} s and {t_dense:.1f} s), "
+                      f"extrapolated linearly to all heads; {cores} host cores in the "
+                      f"process's affinity mask, BLAS pool of {blas} threads"}
 
 
 def _pcts(xs):
@@ -438,20 +456,81 @@ def bench_block_mask(args, isa, torch, q, k, v, c):
                           "mfma_frac": flat_flops / (fl_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
 
 
+def bench_c4_sweep(args, isa, torch, dev):
+    """The N=51200 workload over its whole (alpha_s, alpha_f) grid: per point the
+    ISA latency, the exact path's time and rate, and the Taylor path's time;
+    the library's dense kernel once on the same input."""
+    from synth import CONFIGS, generate_config
+
+    c = CONFIGS["isa_bf16_N51200"]
+    B, H, L_src, L_ctx, D, b = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["block"]
+    N = L_src + L_ctx
+    t0 = time.perf_counter()
+    inp = generate_config("isa_bf16_N51200")
+    _log(f"c4 sweep: generated N={N} in {time.perf_counter() - t0:.1f} s")
+    to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = (to_gpu(inp[x]) for x in ("q", "k", "v"))
+    del inp
+    dense_flops = 4.0 * B * H * N * N * D
+    points = []
+    for a_s in c["sweep_alpha_s"]:
+        for a_f in c["sweep_alpha_f"]:
+            cp = dict(c, alpha_s=a_s, alpha_f=a_f)
+            ms, stage_ms, info = _time_variant(isa, torch, q, k, v, cp, args.c4_steps)
+            ex_flops = 4.0 * B * H * info["n_sharp"] * b * info["l_new"] * D
+            ex_ms = stage_ms["attn_exact"]
+            points.append({"alpha_s": a_s, "alpha_f": a_f, "k": info["k"],
+                           "l_new": info["l_new"], "n_flat": info["n_flat"],
+                           "latency_ms": ms,
+                           "dense_equiv_tflops": dense_flops / (ms * 1e-3) / 1e12,
+                           "attn_exact": {"ms": ex_ms, "algorithmic_tflop": ex_flops / 1e12,
+                                          "mfma_frac": ex_flops / (ex_ms * 1e-3) / 1e12
+                                          / PEAK_BF16_TFLOPS},
+                           "attn_taylor_ms": stage_ms["attn_taylor"],
+                           "pre_stages_ms": sum(stage_ms[x] for x in
+                                                ("pool", "coarse_rowstats", "coarse_colsum",
+                                                 "select_route"))})
+            _log(f"c4 as{a_s} af{a_f}: ISA {ms:.3f} ms, exact {ex_ms:.3f} ms")
+    dense = None
+    if not args.no_dense:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        dms = _timed(torch, lambda: isa.isa_dense_forward(q, k, v, o, lse), args.dense_steps)
+        dense = {"ms": dms, "tflops": dense_flops / (dms * 1e-3) / 1e12,
+                 "mfma_frac": dense_flops / (dms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        for pt in points:
+            pt["speedup_vs_dense"] = dms / pt["latency_ms"]
+        _log(f"c4 dense {dms:.3f} ms")
+    del q, k, v
+    torch.cuda.empty_cache()
+    return {"workload": c["name"], "B": B, "H": H, "N": N, "D": D, "block": b,
+            "steps": args.c4_steps, "points": points, "dense": dense}
+
+
+def _timed(torch, fn, n):
+    """Mean event time of n back-to-back calls after two untimed ones."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 SWEEP_N = (5120, 8192, 16384, 32768, 51200, 65536)
 
 
-def sweep(args):
+def length_sweep(args, torch, isa, dev):
     """ISA forward vs the library's dense attention over the sequence lengths
     the pages work at (5K-50K tokens, about 64K at 544x960): B=1, H=40, D=128,
     L_src = L_ctx = N/2, the 32K workload's ratios, seeded ICL-structured inputs
-    (one seed per N).  Prints one JSON line with one entry per N."""
-    import torch
-
-    import sparse_attention_context_block_amd as isa
+    (one seed per N).  Returns one entry per N."""
     from synth import generate
 
-    dev = torch.device("cuda:0")
     a_s = 0.25 if args.alpha_s is None else args.alpha_s
     a_f = 0.5 if args.alpha_f is None else args.alpha_f
     B, H, D, b = 1, 40, 128, 64
@@ -465,21 +544,10 @@ def sweep(args):
         ws = torch.empty(plan.info["workspace_bytes"], dtype=torch.uint8, device=dev)
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-
-        def timed(fn, n):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(n):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / n
-
-        ims = timed(lambda: isa.isa_forward(plan, q, k, v, o, lse, workspace=ws), args.steps)
-        dms = timed(lambda: isa.isa_dense_forward(q, k, v, o, lse), max(2, args.dense_steps))
+        ims = _timed(torch, lambda: isa.isa_forward(plan, q, k, v, o, lse, workspace=ws),
+                     args.sweep_steps)
+        dms = _timed(torch, lambda: isa.isa_dense_forward(q, k, v, o, lse),
+                     max(2, args.dense_steps))
         dense_flops = 4.0 * B * H * N * N * D
         rows.append({"N": N, "k": plan.info["k"], "l_new": plan.info["l_new"],
                      "isa_ms": ims, "dense_ms": dms, "speedup": dms / ims,
@@ -488,10 +556,19 @@ def sweep(args):
         _log(f"N={N}: ISA {ims:.3f} ms, dense {dms:.3f} ms, speedup {dms / ims:.2f}x")
         del q, k, v, o, lse, ws
         torch.cuda.empty_cache()
-    print(json.dumps({"sweep": "ISA forward vs dense attention", "B": B, "H": H, "D": D,
-                      "block": b, "alpha_s": a_s, "alpha_f": a_f, "steps": args.steps,
-                      "dtype": "bf16", "data": "synthetic (seeded [source|context] generator)",
-                      "rows": rows}), flush=True)
+    return {"sweep": "ISA forward vs dense attention", "B": B, "H": H, "D": D, "block": b,
+            "alpha_s": a_s, "alpha_f": a_f, "steps": args.sweep_steps, "rows": rows}
+
+
+def sweep(args):
+    """--sweep: only the sequence-length sweep, as one JSON line."""
+    import torch
+
+    import sparse_attention_context_block_amd as isa
+
+    out = length_sweep(args, torch, isa, torch.device("cuda:0"))
+    out.update({"dtype": "bf16", "data": "synthetic (seeded [source|context] generator)"})
+    print(json.dumps(out), flush=True)
 
 
 def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_pp_kernel<128, 1>"):
@@ -634,6 +711,13 @@ def main():
         dist = bench_distribution(args, isa, torch, plan, q, k, v, o, lse, ws, dev,
                                   not args.no_dense)
 
+    c4_sweep = None
+    if args.c4_steps > 0:
+        c4_sweep = bench_c4_sweep(args, isa, torch, dev)
+    n_sweep = None
+    if args.sweep_steps > 0:
+        n_sweep = length_sweep(args, torch, isa, dev)
+
     dense_equiv = 4.0 * B * H * N * N * D
     exact_flops = 4.0 * B * H * info["n_sharp"] * b * info["l_new"] * D
     taylor_flops = 4.0 * B * H * info["n_flat"] * b * info["n_kv_blocks"] * D
@@ -644,9 +728,20 @@ def main():
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                 "algorithmic_flops_per_launch": exact_flops, "avg_launch_ms": ex_ms}
+    # the pooling kernel's rate with the caches evicted (every input byte from
+    # HBM) is the headline; the warm rate (inputs partly left in the MALL by the
+    # previous call) beside it
+    pool_cold_ms = dist["stages_cold_median_ms"]["pool"] if dist else None
+    pool_stage = {"ms": stage_ms["pool"],
+                  "GB/s_warm": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9,
+                  "hbm_frac_warm": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "algorithmic_bytes": pool_bytes}
+    if pool_cold_ms:
+        pool_stage.update({"ms_cold": pool_cold_ms,
+                           "GB/s": pool_bytes / (pool_cold_ms * 1e-3) / 1e9,
+                           "hbm_frac": pool_bytes / (pool_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS})
     stages = {
-        "pool": {"ms": stage_ms["pool"], "GB/s": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9,
-                 "hbm_frac": pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "pool": pool_stage,
         # the coarse logits: 2 D fp64 flops per (query block, key block) for the
         # row statistics, per (source block, context block) for the column means
         "coarse_rowstats": _fp64_rate(stage_ms["coarse_rowstats"],
@@ -688,6 +783,8 @@ def main():
         "rope": rope,
         "block_lengths": block_lengths,
         "partial_blocks": partial_blocks,
+        "c4_sweep": c4_sweep,
+        "length_sweep": n_sweep,
         "backward": backward,
         "cpu_baseline": cpu,
     }

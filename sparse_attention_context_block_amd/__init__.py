@@ -26,10 +26,11 @@ STAGE_NAMES = ("pool", "coarse_rowstats", "coarse_colsum", "select_route", "attn
                "attn_taylor")
 _DTYPES = {torch.bfloat16: ISA_DTYPE_BF16, torch.float32: ISA_DTYPE_FP32}
 
-# Every symbol include/isa.h declares.
+# Every symbol include/isa.h declares, and the test hooks of include/isa_testing.h.
 EXPORTS = ("isa_plan_create", "isa_plan_get_info", "isa_plan_destroy", "isa_forward",
-           "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward", "isa_backward_workspace_bytes",
-           "isa_status_string", "isa_last_hip_error", "isa_debug_set_flags")
+           "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward",
+           "isa_backward_workspace_bytes", "isa_status_string", "isa_last_hip_error")
+TESTING_EXPORTS = ("isa_debug_set_flags", "isa_testing_fail_launch")
 
 
 class IsaError(RuntimeError):
@@ -88,9 +89,10 @@ def _lib():
         L.isa_status_string.restype = ctypes.c_char_p
         L.isa_last_hip_error.argtypes = []
         L.isa_debug_set_flags.argtypes = [ctypes.c_uint32]
+        L.isa_testing_fail_launch.argtypes = [i32, i32]
         for name in ("isa_plan_create", "isa_plan_get_info", "isa_plan_destroy", "isa_forward",
                      "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward",
-                     "isa_last_hip_error", "isa_debug_set_flags"):
+                     "isa_last_hip_error", "isa_debug_set_flags", "isa_testing_fail_launch"):
             getattr(L, name).restype = ctypes.c_int
         _L = L
     return _L
@@ -104,13 +106,21 @@ def isa_last_hip_error():
     return int(_lib().isa_last_hip_error())
 
 
+# Test hooks (include/isa_testing.h): not needed to run ISA.
 ISA_DEBUG_GLOBAL_TABLES = 1
 ISA_DEBUG_4WAVE_EXACT = 2
+ISA_DEBUG_PINGPONG_EXACT = 4
 
 
 def isa_debug_set_flags(flags):
-    """Diagnostic switches (include/isa.h isa_debug_set_flags); raises on unknown bits."""
+    """Kernel-path switches (isa_testing.h); raises on unknown bits."""
     _check(_lib().isa_debug_set_flags(int(flags)), "isa_debug_set_flags")
+
+
+def isa_testing_fail_launch(skip, hip_error):
+    """Arm the launch wrapper to report hip_error after `skip` good launches
+    (isa_testing.h); hip_error 0 disarms."""
+    _check(_lib().isa_testing_fail_launch(int(skip), int(hip_error)), "isa_testing_fail_launch")
 
 
 def _check(status, what):
@@ -256,17 +266,39 @@ def isa_dense_forward(q, k, v, o=None, lse=None, stream=None):
     return o, lse
 
 
+def _decision_aux(plan, aux):
+    """isa_aux_t with the forward's decisions sel, flat, sharp for the backward.
+
+    The backward kernels read these ids unchecked, so each must be an int32,
+    contiguous [B, H, count] tensor of this plan (ValueError otherwise) on the
+    GPU (TypeError otherwise)."""
+    d, info = plan.desc, plan.info
+    a = isa_aux_t()
+    counts = {"sel": info["k"], "flat": info["n_flat"], "sharp": info["n_sharp"]}
+    for f, n in counts.items():
+        if f not in aux:
+            raise ValueError(f"aux lacks {f!r}")
+        t = aux[f]
+        shape = (d.B, d.H, n)
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 \
+                or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"aux[{f!r}]: expected contiguous int32 {shape}, got "
+                             f"{getattr(t, 'dtype', type(t))} {tuple(getattr(t, 'shape', ()))}")
+    for f, n in counts.items():
+        if not aux[f].is_cuda:
+            raise TypeError(f"aux[{f!r}] must be a GPU tensor")
+        setattr(a, f, aux[f].data_ptr() if n else None)
+    return a
+
+
 def isa_backward(plan, q, k, v, o, do, lse, aux, workspace=None, stream=None):
     """Gradients (dq, dk, dv) with the forward's decisions (aux) held fixed."""
-    d = plan.desc
+    d, info = plan.desc, plan.info
     shape = (d.B, d.H, d.L_src + d.L_ctx, d.D)
     dt = _torch_dtype(plan)
     ptrs = [_dev(x, dt, shape, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"),
                                                  (do, "do"))]
-    a = isa_aux_t()
-    for f in ("sel", "flat", "sharp"):
-        t = aux[f]
-        setattr(a, f, t.data_ptr() if t.numel() else None)
+    a = _decision_aux(plan, aux)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         nbytes = _lib().isa_backward_workspace_bytes(plan.handle)

@@ -4,12 +4,15 @@
 // order Taylor paths, merge).  Host code only; every step of the path runs in
 // the device kernels of the other files.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <atomic>
 #include <new>
 #include <string.h>
 
 #include "isa_debug.h"
 #include "isa_internal.h"
+#include "isa_testing.h"
 
 namespace isa {
 std::atomic<uint32_t> g_debug_flags{0};
@@ -52,11 +55,34 @@ isa_status_t hip_status(hipError_t e) {
   return ISA_ERR_HIP;
 }
 
-#define ISA_LAUNCH(expr)                        \
-  do {                                          \
-    isa_status_t s_ = hip_status((expr));       \
-    if (s_ != ISA_OK) return s_;                \
+// Failure injection (isa_testing_fail_launch): launches to let through before
+// the failing one, and the error it reports (0: disarmed).
+std::atomic<int32_t> g_fail_skip{0};
+std::atomic<int32_t> g_fail_error{0};
+
+// hipSuccess to go ahead with the next launch, or the injected error (the
+// launch is then not issued and the hook disarms).
+hipError_t injected_failure() {
+  if (g_fail_error.load(std::memory_order_relaxed) == 0) return hipSuccess;
+  if (g_fail_skip.load(std::memory_order_relaxed) > 0) {
+    g_fail_skip.fetch_sub(1, std::memory_order_relaxed);
+    return hipSuccess;
+  }
+  return (hipError_t)g_fail_error.exchange(0, std::memory_order_relaxed);
+}
+
+#define ISA_LAUNCH(expr)                                     \
+  do {                                                       \
+    hipError_t e_ = injected_failure();                      \
+    if (e_ == hipSuccess) e_ = (expr);                       \
+    isa_status_t s_ = hip_status(e_);                        \
+    if (s_ != ISA_OK) return s_;                             \
   } while (0)
+
+bool log_enabled() {
+  const char* v = getenv("ISA_LOG");
+  return v && *v && strcmp(v, "0") != 0;
+}
 
 size_t elt_size(isa_dtype_t t) { return t == ISA_DTYPE_BF16 ? 2 : 4; }
 
@@ -98,10 +124,21 @@ int isa_last_hip_error(void) { return g_last_hip_error; }
 
 isa_status_t isa_debug_set_flags(uint32_t flags) {
   static_assert(isa::kDebugGlobalTables == ISA_DEBUG_GLOBAL_TABLES &&
-                    isa::kDebug4WaveExact == ISA_DEBUG_4WAVE_EXACT,
+                    isa::kDebug4WaveExact == ISA_DEBUG_4WAVE_EXACT &&
+                    isa::kDebugPingPongExact == ISA_DEBUG_PINGPONG_EXACT,
                 "debug flag bits");
   if (flags & ~isa::kDebugAll) return ISA_ERR_INVALID_ARG;
+  if ((flags & isa::kDebug4WaveExact) && (flags & isa::kDebugPingPongExact))
+    return ISA_ERR_INVALID_ARG;
   isa::g_debug_flags.store(flags, std::memory_order_relaxed);
+  return ISA_OK;
+}
+
+isa_status_t isa_testing_fail_launch(int32_t skip, int32_t hip_error) {
+  if (skip < 0 || hip_error < 0) return ISA_ERR_INVALID_ARG;
+  g_fail_error.store(0, std::memory_order_relaxed);
+  g_fail_skip.store(skip, std::memory_order_relaxed);
+  g_fail_error.store(hip_error, std::memory_order_relaxed);
   return ISA_OK;
 }
 
@@ -185,6 +222,16 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   w.kr = p->rope ? take(tokens) : 0;
   w.total = off;
   in.workspace_bytes = off;
+  if (log_enabled())
+    fprintf(stderr,
+            "[isa] plan B=%d H=%d L_src=%d L_ctx=%d D=%d b=%d alpha_s=%g alpha_f=%g "
+            "alpha_ns=%g %s rope_base=%g: n_src=%lld n_ctx=%lld k=%lld N_K'=%lld L_new=%lld "
+            "n_flat=%lld n_sharp=%lld n_ns=%lld workspace=%zu bytes\n",
+            d.B, d.H, d.L_src, d.L_ctx, d.D, d.block, d.alpha_s, d.alpha_f, d.alpha_ns,
+            d.dtype == ISA_DTYPE_BF16 ? "bf16" : "fp32", d.rope_base,
+            (long long)in.n_src_blocks, (long long)in.n_ctx_blocks, (long long)in.k,
+            (long long)in.n_kv_blocks, (long long)in.l_new, (long long)in.n_flat,
+            (long long)in.n_sharp, (long long)in.n_ns, in.workspace_bytes);
   *out = p;
   return ISA_OK;
 }

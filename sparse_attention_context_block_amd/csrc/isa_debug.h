@@ -1,5 +1,5 @@
-// Diagnostic switches set through isa_debug_set_flags (include/isa.h) and read
-// by the kernel launchers.
+// Kernel-path switches set through isa_debug_set_flags (include/isa_testing.h,
+// test hooks only) and read by the kernel launchers.
 #pragma once
 #include <stdint.h>
 
@@ -12,5 +12,8 @@ constexpr uint32_t kDebugGlobalTables = 1u;
 // Matches ISA_DEBUG_4WAVE_EXACT: block-table launches of the bf16 attention
 // (exact path, dense baseline) run on the 4-wave kernel.
 constexpr uint32_t kDebug4WaveExact = 2u;
-constexpr uint32_t kDebugAll = kDebugGlobalTables | kDebug4WaveExact;
+// Matches ISA_DEBUG_PINGPONG_EXACT: the same launches run on the 8-wave
+// ping-pong kernel.
+constexpr uint32_t kDebugPingPongExact = 4u;
+constexpr uint32_t kDebugAll = kDebugGlobalTables | kDebug4WaveExact | kDebugPingPongExact;
 }  // namespace isa

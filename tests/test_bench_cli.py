@@ -24,5 +24,6 @@ def test_help_lists_the_workload_options():
     r = _run("--help")
     assert r.returncode == 0
     for opt in ("--workload", "--bwd-workload", "--partial-shift", "--mask-alpha-ns",
-                "--rope-base", "--block-lengths", "--sweep", "--steps", "--warmup"):
+                "--rope-base", "--block-lengths", "--sweep", "--steps", "--warmup",
+                "--c4-steps", "--sweep-steps"):
         assert opt in r.stdout, opt

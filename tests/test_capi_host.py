@@ -14,10 +14,11 @@ from synth import CONFIGS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "isa.h")
+TESTING_HEADER = os.path.join(ROOT, "include", "isa_testing.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(isa_[a-z_0-9]+)\s*\(", text)))
 
@@ -29,6 +30,12 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), f"{name} declared in include/isa.h but not exported"
     assert sorted(isa.EXPORTS) == declared
+    hooks = _declared_functions(TESTING_HEADER)
+    for name in hooks:
+        assert hasattr(lib, name), f"{name} declared in include/isa_testing.h but not exported"
+    assert sorted(isa.TESTING_EXPORTS) == hooks
+    # the product header declares no global switch
+    assert not set(hooks) & set(declared)
 
 
 def test_debug_flags_accept_known_bits_only():
@@ -36,9 +43,12 @@ def test_debug_flags_accept_known_bits_only():
     isa.isa_debug_set_flags(isa.ISA_DEBUG_GLOBAL_TABLES)
     isa.isa_debug_set_flags(isa.ISA_DEBUG_4WAVE_EXACT)
     isa.isa_debug_set_flags(isa.ISA_DEBUG_GLOBAL_TABLES | isa.ISA_DEBUG_4WAVE_EXACT)
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_GLOBAL_TABLES | isa.ISA_DEBUG_PINGPONG_EXACT)
     isa.isa_debug_set_flags(0)
     with pytest.raises(RuntimeError, match="INVALID_ARG"):
-        isa.isa_debug_set_flags(4)
+        isa.isa_debug_set_flags(8)
+    with pytest.raises(RuntimeError, match="INVALID_ARG"):  # two exact-path kernels at once
+        isa.isa_debug_set_flags(isa.ISA_DEBUG_4WAVE_EXACT | isa.ISA_DEBUG_PINGPONG_EXACT)
     assert isa._lib().isa_debug_set_flags(0x80000000) == 1  # ISA_ERR_INVALID_ARG
     isa.isa_debug_set_flags(0)
 
@@ -268,3 +278,75 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         isa.isa_plan_create(1, 1, 64, 64, 64)
     with pytest.raises(RuntimeError, match="not built"):
         isa._lib()
+
+
+def test_injected_launch_failure_reaches_isa_error():
+    # The launch wrapper's failure hook: the first launch reports hipErrorLaunchFailure
+    # (719) without being issued, so no HIP call happens and no GPU is needed.  The
+    # status must come back as ISA_ERR_HIP, with the HIP code in isa_last_hip_error,
+    # and the binding must turn it into IsaError.
+    lib = isa._lib()
+    p = isa.isa_plan_create(1, 2, 256, 256, 128)
+    fake = ctypes.c_void_p(0x1000)
+    ws = p.info["workspace_bytes"]
+    isa.isa_testing_fail_launch(0, 719)
+    st = lib.isa_forward(p.handle, fake, fake, fake, fake, None, None, fake, ws, None)
+    assert st == isa.ISA_ERR_HIP
+    assert isa.isa_last_hip_error() == 719
+    with pytest.raises(isa.IsaError, match=r"ISA_ERR_HIP.*hipError 719") as e:
+        isa._check(st, "isa_forward")
+    assert e.value.status == isa.ISA_ERR_HIP
+    # the hook fires once: the dense entry point (its first launch) fails the same way
+    isa.isa_testing_fail_launch(0, 98)
+    assert lib.isa_dense_forward(1, 1, 128, 128, 0, fake, fake, fake, fake, None, None) \
+        == isa.ISA_ERR_HIP
+    assert isa.isa_last_hip_error() == 98
+    # invalid arguments to the hook
+    with pytest.raises(isa.IsaError, match="INVALID_ARG"):
+        isa.isa_testing_fail_launch(-1, 5)
+    isa.isa_testing_fail_launch(0, 0)  # disarmed
+
+
+def test_plan_log(tmp_path):
+    # ISA_LOG=1 prints each plan's derived sizes to stderr (in a child process,
+    # so the environment is read fresh)
+    import subprocess
+    import sys
+    code = ("import sparse_attention_context_block_amd as isa; "
+            "isa.isa_plan_create(1, 40, 16384, 16384, 128, 64, 0.25, 0.5)")
+    env = dict(os.environ, ISA_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "[isa] plan" in r.stderr and "k=64" in r.stderr and "L_new=20480" in r.stderr
+    env["ISA_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert "[isa] plan" not in r.stderr
+
+
+def test_backward_binding_validates_decisions():
+    # the backward kernels read sel/flat/sharp unchecked, so the binding refuses
+    # wrong dtypes or shapes (ValueError) and host tensors (TypeError) before
+    # any launch
+    import torch
+    p = isa.isa_plan_create(1, 2, 256, 256, 128)
+    info = p.info
+    shapes = {"sel": (1, 2, info["k"]), "flat": (1, 2, info["n_flat"]),
+              "sharp": (1, 2, info["n_sharp"])}
+    good = {f: torch.zeros(sh, dtype=torch.int32) for f, sh in shapes.items()}
+    for f in shapes:
+        bad = dict(good, **{f: good[f].to(torch.int64)})  # e.g. oracle output moved over
+        with pytest.raises(ValueError, match=f"aux\\['{f}'\\].*int32"):
+            isa._decision_aux(p, bad)
+        bad = dict(good, **{f: torch.zeros(1, 2, shapes[f][2] + 1, dtype=torch.int32)})
+        with pytest.raises(ValueError, match=f"aux\\['{f}'\\]"):
+            isa._decision_aux(p, bad)
+        missing = {g: t for g, t in good.items() if g != f}
+        with pytest.raises(ValueError, match="lacks"):
+            isa._decision_aux(p, missing)
+    with pytest.raises(TypeError, match="GPU"):  # right dtype and shape, host memory
+        isa._decision_aux(p, good)
+    x = torch.zeros(1, 2, 512, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        isa.isa_backward(p, x, x, x, x, x, torch.zeros(1, 2, 512), good)

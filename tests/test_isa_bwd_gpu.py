@@ -98,7 +98,8 @@ def test_backward_workload_b2_n16384():
     got = [out_f64(g) for g in grads]
     for g in got:
         assert np.isfinite(g).all()
-    for bi, h in ((0, 3), (1, 29)):
+    # four heads spanning both batch entries
+    for bi, h in ((0, 3), (0, 22), (1, 11), (1, 29)):
         sl = (slice(bi, bi + 1), slice(h, h + 1))
         ref = orc.isa_ref_bwd(*(to_f64(inp[x][sl], "bf16") for x in ("q", "k", "v", "do")),
                               L_src, L_ctx, 64, aux["sel"][sl], aux["flat"][sl])

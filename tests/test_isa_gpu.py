@@ -245,10 +245,53 @@ def test_workload_n32768_bf16_headline():
     _workload_parity("isa_bf16_N32768", heads_out=4, rows_out=384)
 
 
-def test_workload_n51200_bf16_sweep():
-    inp = generate_config("isa_bf16_N51200")
-    for a_s, a_f in ((0.125, 0.25), (0.25, 0.5), (0.5, 0.75)):
-        _workload_parity("isa_bf16_N51200", a_s, a_f, heads_out=2, rows_out=256, inp=inp)
+_N51200_INPUT = {}
+
+
+def _n51200_input():
+    # one draw of the N=51200 workload serves all nine ratio pairs
+    if "inp" not in _N51200_INPUT:
+        _N51200_INPUT["inp"] = generate_config("isa_bf16_N51200")
+    return _N51200_INPUT["inp"]
+
+
+# The pages sweep the select ratio and the flat ratio one at a time ([summary] 4
+# "Hyperparameters in ISA"; [notes] key findings); this covers the whole grid,
+# from the least exact-path work (alpha_s 0.125, alpha_f 0.75) to the most
+# (alpha_s 0.5, alpha_f 0.25).
+@pytest.mark.parametrize("a_f", CONFIGS["isa_bf16_N51200"]["sweep_alpha_f"])
+@pytest.mark.parametrize("a_s", CONFIGS["isa_bf16_N51200"]["sweep_alpha_s"])
+def test_workload_n51200_bf16_sweep(a_s, a_f):
+    _workload_parity("isa_bf16_N51200", a_s, a_f, heads_out=2, rows_out=256,
+                     inp=_n51200_input())
+
+
+# The sequence-length sweep's shortest and longest inputs (B=1, H=40, D=128,
+# L_src = L_ctx = N/2, ratios of the 32K workload; [notes] research background
+# and [summary] 1: 5K-50K tokens, about 64K at 544x960), drawn as the bench's
+# sweep draws them.
+@pytest.mark.parametrize("N", (5120, 65536))
+def test_sweep_length_parity(N):
+    B, H, D, b, a_s, a_f = 1, 40, 128, 64, 0.25, 0.5
+    seed = 2000 + N // 1024
+    _say(f"sweep length N{N} B{B} H{H} D{D} as{a_s} af{a_f} seed {seed}")
+    inp = generate(B, H, N // 2, N // 2, D, b, seed=seed, variant="icl")
+    plan, o, lse, aux = _run_isa(inp, "bf16", B, H, N // 2, N // 2, D, a_s, a_f)
+    ref = per_head_decisions(inp["q"], inp["k"], "bf16", N // 2, N // 2, b, a_s, a_f)
+    ex = _check_decisions(aux, ref, plan.info)
+    rows = _sample_rows(N, 256, seed)
+    rng = np.random.default_rng(seed + 1)
+    heads = [(0, int(h)) for h in sorted(rng.choice(H, 3, replace=False))]
+    O_ref, L_ref = fixed_ref_rows(inp["q"], inp["k"], inp["v"], "bf16", N // 2, N // 2, b,
+                                  aux["sel"], aux["flat"], rows, heads)
+    O_gpu = out_f64(o)
+    got = np.stack([O_gpu[bi, h, rows] for bi, h in heads])
+    got_l = np.stack([lse[bi, h, rows] for bi, h in heads])
+    mx, mn = check_close(got, O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (sampled rows)")
+    check_close(got_l, L_ref, 5e-3, 1e-3, "LSE (sampled rows)")
+    assert torch.isfinite(o.float()).all()
+    check_in_value_range(o, to_gpu(inp["v"], "bf16"))
+    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e} exemptions sel/route {ex}")
 
 
 def test_workload_b2_n16384_forward():
