@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_exact_isa_bf16_N32768_hbm_traffic.txt")
 # (the kernel's file and the internal header it includes)
 EXACT_KERNEL_SRC = tuple(os.path.join(ROOT, "sparse_attention_context_block_amd", "csrc", f)
-                         for f in ("isa_attn_pp.hip", "isa_internal.h"))
+                         for f in ("isa_attn_w64.hip", "isa_internal.h"))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP64_TFLOPS = 78.6     # MI355X dense fp64
@@ -571,7 +571,7 @@ def sweep(args):
     print(json.dumps(out), flush=True)
 
 
-def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_pp_kernel<128, 1>"):
+def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_w64_kernel<1, false>"):
     """Traffic file text: per-launch HBM bytes of `kernel`, from rocprofv3
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on
     the 256 MiB copy of --calibrate-copy (268435456 bytes read and written)."""
@@ -724,7 +724,7 @@ def main():
     pool_bytes = 3.0 * B * H * N * D * 2 + B * H * info["n_q_blocks"] * D * (8 + 8 + 2 + 2)
     ex_ms = stage_ms["attn_exact"]
     achieved = exact_flops / (ex_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_fwd_pp_kernel<128, 1> (exact path)", "bound": "mfma",
+    roofline = {"kernel": "attn_fwd_w64_kernel<1, false> (exact path)", "bound": "mfma",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                 "algorithmic_flops_per_launch": exact_flops, "avg_launch_ms": ex_ms}

@@ -26,7 +26,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # compiler would otherwise place every MFMA accumulator in AGPRs and copy S, dP
 # and the staging registers between AGPRs and VGPRs on every key tile; the VGPR
 # form keeps the loops free of those copies.
-EXTRA = {"isa_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"isa_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # its direct-to-LDS loads set m0 in inline asm and list it as clobbered,
+         # which the compiler notes (m0 is reserved) on every expansion
+         "isa_attn_w64.hip": ["-Wno-inline-asm"]}
 
 
 def _run(cmd):

@@ -108,9 +108,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream) {
   if (dtype == ISA_DTYPE_BF16) {
-    // block tables (exact path, dense): the ping-pong kernel
-    if (!p.kv_row_table && !(debug_flags() & kDebug4WaveExact)) return launch_attention_pp(p, stream);
-    return launch_attention_bf16(p, stream);
+    // block tables (exact path, dense): the one-wave-per-SIMD kernel where it
+    // applies, else the ping-pong kernel; row tables: the 4-wave kernel
+    const uint32_t dbg = debug_flags();
+    if (p.kv_row_table || (dbg & kDebug4WaveExact)) return launch_attention_bf16(p, stream);
+    if (!(dbg & kDebugPingPongExact) && attention_w64_supported(p))
+      return launch_attention_w64(p, stream);
+    return launch_attention_pp(p, stream);
   }
   if (p.BH == 0 || p.n_q_entries == 0) return hipSuccess;
   dim3 grid(p.n_q_entries, p.BH);

@@ -194,7 +194,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
     for (int i = 0; i < 4; ++i) oacc[j][i] = 0.0f;
   float m_run = -INFINITY;
   float l_run = 0.0f;  // this lane's share of the row sum (reduced at the end)
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One K and one V buffer: K(t+1) is loaded while S(t) runs and stored once
   // every wave is past S(t); V(t+1) is loaded while O += V(t) P(t) runs and
@@ -293,10 +292,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_flat_bf16_kernel(FlatParams 
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * c + h][i], sl2, off));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * c + h][i + 1], sl2, off));
           bf16x2_t pr;
-          pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * c + h][i], sl2, off));
-          pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * c + h][i + 1], sl2, off));
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+          pr[0] = (__bf16)p0;
+          pr[1] = (__bf16)p1;
+          // the row sum adds the fp32 exponentials (a packed bf16 dot product
+          // would issue on the matrix pipe and wait for the MFMAs)
+          l_run = (l_run + p0) + p1;
           pk[c][4 * h + i] = pr[0];
           pk[c][4 * h + i + 1] = pr[1];
         }

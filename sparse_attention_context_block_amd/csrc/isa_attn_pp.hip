@@ -233,7 +233,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
   float m_run = -INFINITY;
   float l_run = 0.0f;
   const float sl2 = p.scale_log2;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   f32x16_t sacc[2];
   bf16x8_t pk[4];
 
@@ -297,7 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pp_kernel(AttnParams p) 
         bf16x2_t pr;
         pr[0] = (__bf16)p0;
         pr[1] = (__bf16)p1;
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+        // the row sum adds the fp32 exponentials (a packed bf16 dot product
+        // would issue on the matrix pipe and wait for the MFMAs)
+        l_run = (l_run + p0) + p1;
         pk[c][e2] = pr[0];
         pk[c][e2 + 1] = pr[1];
       }

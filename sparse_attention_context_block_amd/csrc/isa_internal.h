@@ -150,10 +150,14 @@ struct AttnParams {
 
 hipError_t launch_attention(const AttnParams& p, isa_dtype_t dtype, hipStream_t stream);
 
-// bf16 kernels: the 4-wave kernel (any key source; used for row tables) and
-// the 8-wave ping-pong kernel (whole 64-row key tiles: exact path, dense).
+// bf16 kernels: the 4-wave kernel (any key source; used for row tables), the
+// one-wave-per-SIMD kernel (block tables at D = 128 with 64- or 128-token
+// blocks: exact path, dense) and the 8-wave ping-pong kernel (the other block
+// tables: D = 64, 32-token blocks).
 hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attention_pp(const AttnParams& p, hipStream_t stream);
+bool attention_w64_supported(const AttnParams& p);
+hipError_t launch_attention_w64(const AttnParams& p, hipStream_t stream);
 
 // Flat query blocks with a block mask (alpha_ns > 0): per flat block, the
 // K_new blocks listed in ns token by token, every other block of K_new through

@@ -119,3 +119,68 @@ def test_4wave_dense_matches_oracle(D):
     # ping-pong kernel: identical bits
     assert torch.equal(o4, od) and torch.equal(l4, ld)
     _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}; equal to the ping-pong kernel")
+
+
+# The one-wave-per-SIMD kernel (the default for block tables at D = 128 with
+# 64- and 128-token blocks) against the 8-wave ping-pong kernel
+# (ISA_DEBUG_PINGPONG_EXACT): the same keys in the same tile order, the same
+# per-row exponentials, running-max updates and row sums, and the same product
+# order into O, so the two must agree bit for bit.  The cases cover one to
+# five key tiles (the three-tile prefetch ring and the tiles past the end),
+# odd and even tile counts (the loop body runs two tiles per trip), both block
+# lengths, and partial tiles.
+def _isa_both(inp, L_src, L_ctx, b, a_s, a_f):
+    def run():
+        plan = isa.isa_plan_create(1, 2, L_src, L_ctx, 128, b, a_s, a_f, dtype=torch.bfloat16)
+        q, k, v = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v"))
+        o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
+        torch.cuda.synchronize()
+        return o, lse, aux
+    o1, l1, a1 = run()
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_PINGPONG_EXACT)
+    try:
+        o2, l2, a2 = run()
+    finally:
+        isa.isa_debug_set_flags(0)
+    for key in a1:
+        assert torch.equal(a1[key], a2[key]), key
+    return (o1, l1), (o2, l2)
+
+
+@pytest.mark.parametrize("b,L_src,L_ctx,a_s,a_f,seed", [
+    (64, 1024, 1024, 0.25, 0.5, 321),    # aligned, 20 key tiles
+    (64, 1088, 960, 0.25, 0.5, 322),     # aligned, 21 key tiles (odd)
+    (128, 1024, 1024, 0.5, 0.25, 323),   # 128-token blocks
+    (64, 1000, 700, 0.5, 0.5, 324),      # partial tiles (tails 40 and 60)
+    (128, 1000, 700, 0.5, 0.0, 325),     # partial and empty half tiles
+    (64, 64, 64, 1.0, 0.0, 326),         # two key tiles
+    (64, 128, 64, 0.0, 0.0, 327),        # two key tiles, nothing kept
+    (64, 64, 0, 0.0, 0.0, 328),          # one key tile
+])
+def test_w64_exact_path_equals_pingpong(b, L_src, L_ctx, a_s, a_f, seed):
+    _say(f"w64 vs ping-pong B1 H2 L_src{L_src} L_ctx{L_ctx} D128 b{b} as{a_s} af{a_f} seed{seed}")
+    inp = generate(1, 2, L_src, L_ctx, 128, b, seed=seed, variant="icl")
+    (o1, l1), (o2, l2) = _isa_both(inp, L_src, L_ctx, b, a_s, a_f)
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+    _say("ok bit-identical")
+
+
+@pytest.mark.parametrize("N", [64, 128, 192, 320, 2048])
+def test_w64_dense_equals_pingpong_and_oracle(N):
+    seed = 330 + N // 64
+    _say(f"w64 dense bf16 B1 H2 N{N} D128 seed{seed}")
+    inp = generate(1, 2, N, 0, 128, 64, seed=seed, variant="plain")
+    q, k, v = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v"))
+    o1, l1 = isa.isa_dense_forward(q, k, v)
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_PINGPONG_EXACT)
+    try:
+        o2, l2 = isa.isa_dense_forward(q, k, v)
+    finally:
+        isa.isa_debug_set_flags(0)
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.dense_ref(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v")))
+    mx, mn = check_close(out_f64(o1), O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (w64 dense)")
+    check_close(l1.cpu().numpy(), L_ref, 5e-3, 1e-3, "LSE (w64 dense)")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}; equal to the ping-pong kernel")
