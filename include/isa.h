@@ -168,6 +168,31 @@ isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   void* const* events);
 
+/* Largest plan workspace (info.workspace_bytes) isa_forward_noalloc serves:
+ * 128 MiB, e.g. B * H = 40 heads of D = 128 up to N = 65536 without the block
+ * mask or the rotary embedding. */
+#define ISA_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+/* isa_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same launches as isa_forward, with the workspace taken from an array of
+ * ISA_STATIC_WORKSPACE_BYTES that the library holds on each device it runs on
+ * (reserved when the library's device code is loaded on that device, kept
+ * until the process ends).  No hipMalloc, hipFree or other allocating call;
+ * the caller still passes Q, K, V, O, lse and aux as for isa_forward.  The
+ * first call on a device resolves the array's address there (on the device of
+ * `stream`, or the current device for the NULL stream).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on a device (other streams, other
+ * threads) race and give wrong results; calls ordered on one stream are safe.
+ * Nothing needs clearing between calls: the forward writes every workspace
+ * byte before it reads it.
+ * Errors: as isa_forward; ISA_ERR_WORKSPACE when info.workspace_bytes exceeds
+ * ISA_STATIC_WORKSPACE_BYTES (checked first, on the host); ISA_ERR_HIP when
+ * the device or the array's address cannot be resolved. */
+isa_status_t isa_forward_noalloc(isa_plan_t plan, const void* Q, const void* K, const void* V,
+                                 void* O, float* lse, const isa_aux_t* aux, void* stream);
+
 /* The gather + concat of Context Pre-Selection ([notes] key design 1;
  * [summary] 3 Pre-Selection), materialised: K_new, V_new [B, H, l_new, D] =
  * [all source tokens ; tokens of the context blocks listed in sel, in the

@@ -22,13 +22,14 @@ LIB_PATH = os.path.join(_PKG, "libisa.so")
 ISA_OK, ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED, ISA_ERR_WORKSPACE, ISA_ERR_HIP = range(5)
 ISA_DTYPE_BF16, ISA_DTYPE_FP32 = 0, 1
 ISA_PROFILE_STAGES = 6
+ISA_STATIC_WORKSPACE_BYTES = 128 << 20
 STAGE_NAMES = ("pool", "coarse_rowstats", "coarse_colsum", "select_route", "attn_exact",
                "attn_taylor")
 _DTYPES = {torch.bfloat16: ISA_DTYPE_BF16, torch.float32: ISA_DTYPE_FP32}
 
 # Every symbol include/isa.h declares, and the test hooks of include/isa_testing.h.
 EXPORTS = ("isa_plan_create", "isa_plan_get_info", "isa_plan_destroy", "isa_forward",
-           "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward",
+           "isa_forward_profiled", "isa_forward_noalloc", "isa_gather", "isa_dense_forward", "isa_backward",
            "isa_backward_workspace_bytes", "isa_status_string", "isa_last_hip_error")
 TESTING_EXPORTS = ("isa_debug_set_flags", "isa_testing_fail_launch")
 
@@ -79,6 +80,7 @@ def _lib():
         L.isa_forward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(isa_aux_t), vp, sz, vp]
         L.isa_forward_profiled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(isa_aux_t),
                                            vp, sz, vp, ctypes.POINTER(vp)]
+        L.isa_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(isa_aux_t), vp]
         L.isa_gather.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.isa_dense_forward.argtypes = [i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp]
         L.isa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(isa_aux_t),
@@ -91,7 +93,7 @@ def _lib():
         L.isa_debug_set_flags.argtypes = [ctypes.c_uint32]
         L.isa_testing_fail_launch.argtypes = [i32, i32]
         for name in ("isa_plan_create", "isa_plan_get_info", "isa_plan_destroy", "isa_forward",
-                     "isa_forward_profiled", "isa_gather", "isa_dense_forward", "isa_backward",
+                     "isa_forward_profiled", "isa_forward_noalloc", "isa_gather", "isa_dense_forward", "isa_backward",
                      "isa_last_hip_error", "isa_debug_set_flags", "isa_testing_fail_launch"):
             getattr(L, name).restype = ctypes.c_int
         _L = L
@@ -228,6 +230,39 @@ def isa_forward(plan, q, k, v, o=None, lse=None, aux=False, workspace=None, stre
         arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
         _check(_lib().isa_forward_profiled(*args, arr), "isa_forward_profiled")
     return o, lse, out_aux
+
+
+def isa_forward_noalloc(plan, q, k, v, o, lse=None, aux=None, stream=None):
+    """The ISA forward with the library's static per-device workspace
+    (isa_forward_noalloc): allocates nothing, so every output is the caller's.
+    ``o``: [B, H, N, D]; ``lse``: [B, H, N] float32 or None (not written);
+    ``aux``: None or a dict of preallocated decision tensors, any subset of
+    the keys isa_forward(aux=True) returns, with the same dtypes and shapes.
+    Plans whose workspace_bytes exceed ISA_STATIC_WORKSPACE_BYTES raise
+    IsaError (ISA_ERR_WORKSPACE).  Calls that overlap on one device race."""
+    d, info = plan.desc, plan.info
+    N = d.L_src + d.L_ctx
+    shape = (d.B, d.H, N, d.D)
+    dt = _torch_dtype(plan)
+    ptrs = [_dev(x, dt, shape, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lse_p = None if lse is None else _dev(lse, torch.float32, shape[:3], "lse")
+    a = isa_aux_t()
+    if aux:
+        bh = (d.B, d.H)
+        spec = dict(sel=(torch.int32, bh + (info["k"],)),
+                    flat=(torch.int32, bh + (info["n_flat"],)),
+                    sharp=(torch.int32, bh + (info["n_sharp"],)),
+                    ctx_score=(torch.float64, bh + (info["n_ctx_blocks"],)),
+                    sharpness=(torch.float64, bh + (info["n_q_blocks"],)),
+                    ns=(torch.int32, bh + (info["n_flat"], info["n_ns"])))
+        for f, t in aux.items():
+            if f not in spec:
+                raise ValueError(f"aux: unknown field {f!r}")
+            dtype_f, shape_f = spec[f]
+            setattr(a, f, _dev(t, dtype_f, shape_f, f"aux[{f!r}]") if t.numel() else None)
+    _check(_lib().isa_forward_noalloc(plan.handle, *ptrs, lse_p, ctypes.byref(a),
+                                      _stream(stream)), "isa_forward_noalloc")
+    return o, lse
 
 
 def isa_gather(plan, k, v, sel, k_new=None, v_new=None, stream=None):

@@ -1,7 +1,8 @@
 // C-ABI host layer: plan validation, workspace layout and the launch
 // sequence of the ISA forward ([notes] overall framework: pooling attention,
 // Context Pre-Selection, grouping by query sharpness, the exact and the 0-th
-// order Taylor paths, merge).  Host code only; every step of the path runs in
+// order Taylor paths, merge).  Host code only (plus the device array that
+// serves as isa_forward_noalloc's workspace); every step of the path runs in
 // the device kernels of the other files.
 #include <math.h>
 #include <stdio.h>
@@ -405,6 +406,42 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   return ISA_OK;
 }
 
+// ---- the workspace of isa_forward_noalloc ----
+// One copy per device: a device variable of this code object, reserved when
+// the code object is loaded on a device.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current, and
+// only that address is ever handed to a kernel.
+constexpr size_t kStaticWorkspaceBytes = ISA_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The array's address on the device of `stream` (the current device for the
+// NULL stream).  Concurrent first calls resolve the same address.
+isa_status_t static_workspace(hipStream_t stream, void** out) {
+  int cur = -1;
+  isa_status_t st = hip_status(hipGetDevice(&cur));
+  if (st != ISA_OK) return st;
+  int dev = cur;
+  if (stream && (st = hip_status(hipStreamGetDevice(stream, &dev))) != ISA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return ISA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (dev != cur && (st = hip_status(hipSetDevice(dev))) != ISA_OK) return st;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (dev != cur) {
+      const isa_status_t back = hip_status(hipSetDevice(cur));
+      if (st == ISA_OK) st = back;
+    }
+    if (st != ISA_OK) return st;
+    if (!p) return ISA_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,6 +457,17 @@ isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K,
                                   size_t workspace_bytes, void* stream, void* const* events) {
   if (!events) return ISA_ERR_INVALID_ARG;
   return forward_impl(plan, Q, K, V, O, lse, aux, workspace, workspace_bytes, stream, events);
+}
+
+isa_status_t isa_forward_noalloc(isa_plan_t plan, const void* Q, const void* K, const void* V,
+                                 void* O, float* lse, const isa_aux_t* aux, void* stream) {
+  if (!plan) return ISA_ERR_INVALID_ARG;
+  if (plan->ws.total > kStaticWorkspaceBytes) return ISA_ERR_WORKSPACE;
+  if (plan->BH == 0) return ISA_OK;
+  void* ws = nullptr;
+  const isa_status_t st = static_workspace(static_cast<hipStream_t>(stream), &ws);
+  if (st != ISA_OK) return st;
+  return forward_impl(plan, Q, K, V, O, lse, aux, ws, kStaticWorkspaceBytes, stream, nullptr);
 }
 
 isa_status_t isa_gather(isa_plan_t plan, const void* K, const void* V, const int32_t* sel,

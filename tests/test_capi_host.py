@@ -257,6 +257,7 @@ def test_empty_problem_is_a_no_op():
     p = isa.isa_plan_create(0, 4, 256, 256, 128)
     assert p.info["workspace_bytes"] >= 0
     assert lib.isa_forward(p.handle, None, None, None, None, None, None, None, 0, None) == isa.ISA_OK
+    assert lib.isa_forward_noalloc(p.handle, None, None, None, None, None, None, None) == isa.ISA_OK
     assert lib.isa_dense_forward(0, 3, 128, 128, 0, None, None, None, None, None, None) == isa.ISA_OK
 
 
@@ -350,3 +351,24 @@ def test_backward_binding_validates_decisions():
     x = torch.zeros(1, 2, 512, 128, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         isa.isa_backward(p, x, x, x, x, x, torch.zeros(1, 2, 512), good)
+
+
+def test_noalloc_forward_limit_checked_on_the_host():
+    """isa_forward_noalloc refuses a plan whose workspace exceeds the static
+    array before any HIP call (so this runs without a GPU); the bound in the
+    binding matches the header's."""
+    text = open(HEADER).read()
+    assert re.search(r"#define ISA_STATIC_WORKSPACE_BYTES \(\(size_t\)128 << 20\)", text)
+    assert isa.ISA_STATIC_WORKSPACE_BYTES == 128 << 20
+    lib = isa._lib()
+    assert lib.isa_forward_noalloc(None, None, None, None, None, None, None, None) \
+        == isa.ISA_ERR_INVALID_ARG
+    # the rotated Q and K live in the workspace: 2 x 40 x 32768 x 128 x 2 bytes alone
+    big = isa.isa_plan_create(1, 40, 16384, 16384, 128, rope_base=10000.0)
+    assert big.info["workspace_bytes"] > isa.ISA_STATIC_WORKSPACE_BYTES
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.isa_forward_noalloc(big.handle, fake, fake, fake, fake, None, None, None) \
+        == isa.ISA_ERR_WORKSPACE
+    # the headline shape fits
+    head = isa.isa_plan_create(1, 40, 16384, 16384, 128)
+    assert head.info["workspace_bytes"] <= isa.ISA_STATIC_WORKSPACE_BYTES
