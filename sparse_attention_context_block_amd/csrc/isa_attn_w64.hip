@@ -453,13 +453,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
   //                 with the partner lane; compare and ballot; new max; 2^(old -
   //                 new); and, after tile t-1's last pair and before tile t's
   //                 first, l *= alpha (slot 21)
-  //   slots 48-57   loads of tile t + 3, one per slot
+  //   odd slots 21-39  loads of tile t + 3, one per slot (into the ring slots
+  //                 of K(t) and V(t-2), which no wave reads after the last barrier)
   // Fragment reads run three fragments (six slots) ahead of their products.
   auto iteration = [&](int t, auto par_c) __attribute__((always_inline)) {
     constexpr int P = decltype(par_c)::value;  // parity of tile t
     constexpr int Q = P ^ 1;                   // of tiles t - 1 and t + 1
-    // tile t + 3 is requested in slots 48-57 (its block id was read at the end
-    // of the last iteration)
+    // tile t + 3 is requested in odd slots 21-39 (its block id was read at the
+    // end of the last iteration)
     const Dma dma = dma_plan(id_t3, t + 3);
     const int cnt_next = tile_of(id_t1, min(t + 1, n_tiles - 1)).cnt;
     const uint32_t vprev = lane_addr(v_lane, kVBase + ((t + kNV - 1) % kNV) * kVTile);
@@ -553,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
         for (int h = 0; h < 2; ++h) tmax[h] = -INFINITY;
       }
       if constexpr (slot >= 49 && (slot & 1) == 1) max_step(Q, 0, (slot - 49) >> 1);
-      if constexpr (slot >= 48 && slot < 58) dma_issue(dma, slot - 48);
+      if constexpr (slot >= 21 && slot < 40 && (slot & 1) == 1) dma_issue(dma, (slot - 21) >> 1);
       fence();
     });
     cnt_cur = cnt_next;
@@ -584,6 +585,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
   // accumulator before its product (inline asm, of unknown latency) wrote it.
   auto tail = [&](auto par_c) __attribute__((always_inline)) {
     constexpr int Q = decltype(par_c)::value;  // parity of tile n - 1
+    // The paths into the tail may keep O in other registers; the copies the
+    // compiler then places at the join must land before the first product
+    // reads O (inline asm: the compiler inserts no wait states for it).
+    wait_o(oacc);
     const uint32_t vlast = lane_addr(v_lane, kVBase + ((n_tiles - 1) % kNV) * kVTile);
     bf16x8_t vf[16];
     vf[0] = v_frag(vlast, 0);
