@@ -78,15 +78,16 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u4;
 
-// 16 bytes per lane from sbase + voff into LDS at m0 + 16 * lane (one wait
-// state between the write of m0 and the load that reads it).  The load counts
-// in vmcnt only; the caller waits on it before the barrier that publishes the
-// tile.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+// 16 bytes per lane from sbase + voff into LDS at m0 + 16 * lane, with
+// m0 = lds + LdsOff written in the same statement (one wait state between the
+// write of m0 and the load that reads it).  The load counts in vmcnt only; the
+// caller waits on it before the barrier that publishes the tile.
+template <uint32_t LdsOff>
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
+               : "v"(voff), "s"(sbase), "s"(lds), "n"(LdsOff)
+               : "memory", "m0", "scc");
 }
 
 // O^T (32 dims x 32 queries) += V^T fragment x P^T fragment, accumulator in AGPRs.
@@ -258,23 +259,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     d.last = (uint32_t)max(tl.cnt - 1, 0);
     return d;
   };
-  auto dma_issue = [&](const Dma& d, int i) __attribute__((always_inline)) {
+  auto dma_issue = [&](const Dma& d, auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
     // rows past the tile's valid rows repeat its last one (they are masked)
     auto clamp = [&](uint32_t vo) { return min(vo >> 8, d.last) * 256u + (vo & 255u); };
-    const bool k = i < 4 || i == 9;
-    const int ii = i < 4 ? i : (i == 9 ? 4 : i - 4);
+    constexpr bool k = i < 4 || i == 9;
+    constexpr int ii = i < 4 ? i : (i == 9 ? 4 : i - 4);
     const uint32_t vo = k ? voff_k[ii] : voff_v[ii];
-    const uint32_t m0 = (k ? d.km0 : d.vm0) + 4096 * ii;
     if (i == 9 && wave != 0) return;
     if (d.full)
-      dma16(k ? d.kb : d.vb, vo, m0);
+      dma16<4096 * ii>(k ? d.kb : d.vb, vo, k ? d.km0 : d.vm0);
     else
-      dma16(k ? d.kb : d.vb, clamp(vo), m0);
+      dma16<4096 * ii>(k ? d.kb : d.vb, clamp(vo), k ? d.km0 : d.vm0);
   };
   auto dma_tile = [&](int blk, int u) __attribute__((always_inline)) {
     const Dma d = dma_plan(blk, u);
-#pragma unroll
-    for (int i = 0; i < 10; ++i) dma_issue(d, i);
+    static_for<0, 10>([&](auto i_c) __attribute__((always_inline)) { dma_issue(d, i_c); });
   };
   // Loads per tile: 9 per wave (10 for wave 0).  vmcnt <= 9 leaves the most
   // recent tile in flight and completes every earlier one (wave 0 also waits
@@ -554,7 +554,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
         for (int h = 0; h < 2; ++h) tmax[h] = -INFINITY;
       }
       if constexpr (slot >= 49 && (slot & 1) == 1) max_step(Q, 0, (slot - 49) >> 1);
-      if constexpr (slot >= 21 && slot < 40 && (slot & 1) == 1) dma_issue(dma, (slot - 21) >> 1);
+      if constexpr (slot >= 21 && slot < 40 && (slot & 1) == 1)
+        dma_issue(dma, std::integral_constant<int, ((slot - 21) >> 1)>{});
       fence();
     });
     cnt_cur = cnt_next;
