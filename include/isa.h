@@ -169,8 +169,8 @@ isa_status_t isa_forward_profiled(isa_plan_t plan, const void* Q, const void* K,
                                   void* const* events);
 
 /* Largest plan workspace (info.workspace_bytes) isa_forward_noalloc serves:
- * 128 MiB, e.g. B * H = 40 heads of D = 128 up to N = 65536 without the block
- * mask or the rotary embedding. */
+ * 128 MiB, e.g. B * H = 40 heads of D = 128 up to N = 65536 without the
+ * rotary embedding (whose rotated Q and K live in the workspace). */
 #define ISA_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
 
 /* isa_forward for callers that cannot allocate device memory: code under HIP

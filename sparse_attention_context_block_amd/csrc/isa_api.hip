@@ -24,7 +24,7 @@ using namespace isa;
 
 struct WorkspaceLayout {
   size_t qc, kc, kc_lp, vc_lp, rowmax, rowsum, sharpness, ctx_score, sel, flat, sharp, kv_tab;
-  size_t logits, ns;  // only with n_ns > 0 and n_flat > 0
+  size_t ns;          // only with n_ns > 0 and n_flat > 0
   size_t qr, kr;      // only with the rotary embedding: rotated Q, K
   size_t total;
 };
@@ -216,7 +216,6 @@ isa_status_t isa_plan_create(isa_plan_t* out, const isa_plan_desc_t* desc) {
   w.sharp = take((size_t)BH * in.n_sharp * sizeof(int32_t));
   w.kv_tab = take((size_t)BH * in.n_kv_blocks * sizeof(int32_t));
   const bool masked = in.n_ns > 0 && in.n_flat > 0;
-  w.logits = masked ? take((size_t)BH * in.n_q_blocks * in.n_q_blocks * sizeof(double)) : 0;
   w.ns = masked ? take((size_t)BH * in.n_flat * in.n_ns * sizeof(int32_t)) : 0;
   const size_t tokens = (size_t)BH * p->N * d.D * elt_size(d.dtype);
   w.qr = p->rope ? take(tokens) : 0;
@@ -286,7 +285,6 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
   int32_t* sharp = (aux && aux->sharp) ? aux->sharp : reinterpret_cast<int32_t*>(w + L.sharp);
   int32_t* kv_tab = reinterpret_cast<int32_t*>(w + L.kv_tab);
   const bool masked = in.n_ns > 0 && in.n_flat > 0;
-  double* logits = masked ? reinterpret_cast<double*>(w + L.logits) : nullptr;
   int32_t* ns = !masked ? nullptr
                         : (aux && aux->ns) ? aux->ns : reinterpret_cast<int32_t*>(w + L.ns);
   const int BH = plan->BH, D = d.D, N = (int)plan->N;
@@ -311,7 +309,7 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
     K = kr;
   }
   ISA_STAGE(1);
-  ISA_LAUNCH(launch_coarse_rowstats(qc, kc, BH, n_q, D, rowmax, rowsum, sharpness, logits, s));
+  ISA_LAUNCH(launch_coarse_rowstats(qc, kc, BH, n_q, D, rowmax, rowsum, sharpness, s));
   ISA_STAGE(2);
   ISA_LAUNCH(launch_coarse_colsum(qc, kc, rowmax, rowsum, BH, n_q, n_src, n_ctx, D, ctx_score,
                                   s));
@@ -321,7 +319,7 @@ isa_status_t forward_impl(isa_plan_t plan, const void* Q, const void* K, const v
                                  (int)in.n_flat, sel, flat, sharp, kv_tab, s));
   //    block mask of the flat query blocks: their top n_ns blocks of K_new
   if (masked)
-    ISA_LAUNCH(launch_ns_select(logits, flat, kv_tab, BH, n_q, (int)in.n_flat,
+    ISA_LAUNCH(launch_ns_select(qc, kc, flat, kv_tab, BH, n_q, D, (int)in.n_flat,
                                 (int)in.n_kv_blocks, (int)in.n_ns, ns, s));
   ISA_STAGE(4);
 

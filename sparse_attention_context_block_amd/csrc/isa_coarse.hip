@@ -146,8 +146,7 @@ __device__ inline RowStat stat_merge(const RowStat& a, const RowStat& b) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void rowstats_kernel(
     const double* __restrict__ qc, const double* __restrict__ kc, int n_q, double scale,
-    double* __restrict__ rowmax, double* __restrict__ rowsum, double* __restrict__ sharpness,
-    double* __restrict__ logits) {
+    double* __restrict__ rowmax, double* __restrict__ rowsum, double* __restrict__ sharpness) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[4][WaveTile<D>::kBytes];
   __shared__ RowStat part[4][kTile];
   const int64_t bh = blockIdx.y;
@@ -200,8 +199,6 @@ __global__ __launch_bounds__(kThreads, 2) void rowstats_kernel(
     if (col_ok) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = r0 + g + 4 * r;
-        if (logits && row < n_q) logits[(bh * n_q + row) * (int64_t)n_q + col] = xs[r];
         stat_accumulate(st[r], xs[r]);
       }
     }
@@ -314,16 +311,16 @@ __global__ __launch_bounds__(kThreads, 2) void colsum_kernel(
 
 hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
                                   double* rowmax, double* rowsum, double* sharpness,
-                                  double* logits, hipStream_t stream) {
+                                  hipStream_t stream) {
   if (BH == 0 || n_q == 0) return hipSuccess;
   dim3 grid((n_q + kTile - 1) / kTile, BH);
   const double scale = 1.0 / sqrt((double)D);
   if (D == 128)
     hipLaunchKernelGGL(rowstats_kernel<128>, grid, dim3(kThreads), 0, stream, qc, kc, n_q, scale,
-                       rowmax, rowsum, sharpness, logits);
+                       rowmax, rowsum, sharpness);
   else
     hipLaunchKernelGGL(rowstats_kernel<64>, grid, dim3(kThreads), 0, stream, qc, kc, n_q, scale,
-                       rowmax, rowsum, sharpness, logits);
+                       rowmax, rowsum, sharpness);
   return hipGetLastError();
 }
 

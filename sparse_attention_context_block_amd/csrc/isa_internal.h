@@ -185,9 +185,9 @@ struct FlatParams {
   BlockGrid grid;           // token layout of the blocks (partial segment tails)
 };
 hipError_t launch_attention_flat(const FlatParams& p, isa_dtype_t dtype, hipStream_t stream);
-hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int32_t* kv_tab,
-                            int BH, int n_q, int n_flat, int n_kv, int n_ns, int32_t* ns,
-                            hipStream_t stream);
+hipError_t launch_ns_select(const double* qc, const double* kc, const int32_t* flat,
+                            const int32_t* kv_tab, int BH, int n_q, int D, int n_flat, int n_kv,
+                            int n_ns, int32_t* ns, hipStream_t stream);
 
 // Frequencies of the rotary embedding, base^(-2i/D) for the D/2 pairs
 // (computed on the host, passed by value).
@@ -204,7 +204,7 @@ hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t 
 
 hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
                                   double* rowmax, double* rowsum, double* sharpness,
-                                  double* logits, hipStream_t stream);
+                                  hipStream_t stream);
 
 hipError_t launch_coarse_colsum(const double* qc, const double* kc, const double* rowmax,
                                 const double* rowsum, int BH, int n_q, int n_src, int n_ctx,

@@ -23,6 +23,7 @@ namespace isa {
 namespace {
 
 constexpr int kThreads = 256;
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline uint64_t order_key(double x) {
   const uint64_t u = __double_as_longlong(x);
@@ -107,54 +108,226 @@ __global__ __launch_bounds__(kThreads) void select_route_kernel(
   compact(flag, n_q, flat + bh * n_flat, sharp + bh * (int64_t)(n_q - n_flat), counts);
 }
 
-// Byte offset of the per-wave counts after key[n] (8 bytes each) and flag[n].
-__host__ __device__ inline int ns_counts_offset(int n) { return (9 * n + 15) & ~15; }
+// Block mask of the flat query blocks ([notes] key design 2; the mask is read
+// off the coarse map, [summary] 2 "Pooling Attention"): for flat block i, rank
+// the n_kv blocks of K_new by the coarse logit x_i,kv_tab[u] = Q^c_i .
+// K^c_kv_tab[u] / sqrt(D) (descending; the coarse probability is increasing in
+// x), ties to the smaller position u, and keep the first n_ns, listed
+// ascending.  One workgroup per (G consecutive flat entries, head): G = 4
+// while the keys of the G rows fit 64 KB of LDS with the rest, else 1.
+//
+// The logits are computed here, in fp64 from the pooled rows, for the n_kv
+// blocks each row ranks only (no [N_Q, N_Q] logit matrix is stored).  16 lanes
+// share a pooled key row: each sums D / 16 consecutive dims with fused
+// multiply-adds for every flat row of the workgroup, then a fixed-order
+// butterfly over the 16 lanes.  The sum runs in another order than the coarse
+// map's MFMA tiles, so a logit may differ from the one behind the statistics
+// in its last bits; only near-ties can rank differently.
+//
+// Selection: each wave takes one of the workgroup's rows, with no workgroup
+// barrier.  A radix select over the 64-bit order keys finds the n_ns-th
+// largest key K* exactly, 8 bits per pass from the top (a wave-private 256-bin
+// histogram of the keys that still match the digits found so far; the wave
+// then locates the bin that holds the wanted rank).  Kept: every key above K*,
+// and of the keys equal to K* the ones with the smallest positions, as many
+// as are still wanted.  The kept positions are then listed ascending with a
+// wave prefix scan.
 
-// Block mask of one flat query block i ([notes] key design 2; the mask is
-// read off the coarse map, [summary] 2 "Pooling Attention"): rank the n_kv
-// blocks of K_new by x_i,kv_tab[u] (descending; the coarse probability is
-// increasing in x), ties to the smaller position u, and keep the first n_ns,
-// listed ascending.  One workgroup per (flat entry, head).
+// LDS layout for G rows: keys [G][n] (8 bytes each), block table [n], per-wave
+// histograms [4][256].
+__host__ __device__ inline int ns_tab_offset(int G, int n) { return 8 * G * n; }
+__host__ __device__ inline int ns_hist_offset(int G, int n) {
+  return (ns_tab_offset(G, n) + 4 * n + 15) & ~15;
+}
+__host__ __device__ inline int ns_lds_bytes(int G, int n) {
+  return ns_hist_offset(G, n) + 4 * 256 * (kThreads / 64);
+}
+
+// Orders the wave's LDS accesses: its lanes' LDS operations execute in order,
+// and the fence keeps the compiler from moving one lane's reads above another
+// lane's writes.
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
+// One wave: the n_ns largest of key[0..n) (ties to the smaller position),
+// written ascending to out[0..n_ns).
+__device__ void wave_top(const uint64_t* key, int n, int n_ns, int32_t* hist, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint64_t prefix = 0, mask = 0;
+  int want = n_ns;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+    wave_fence();
+    for (int u = lane; u < n; u += 64) {
+      const uint64_t k = key[u];
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    }
+    wave_fence();
+    // lane l owns bins 4 l .. 4 l + 3 (higher lanes: larger digits)
+    const int b0 = hist[4 * lane], b1 = hist[4 * lane + 1], b2 = hist[4 * lane + 2],
+              b3 = hist[4 * lane + 3];
+    const int own = b0 + b1 + b2 + b3;
+    int above = own;  // keys in the bins of lanes l .. 63
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_down(above, off);
+      if (lane + off < 64) above += y;
+    }
+    const int higher = above - own;
+    // exactly one lane holds the wanted rank: higher < want <= above
+    int d = 0, acc = 0;
+    const bool mine = higher < want && want <= above;
+    if (mine) {
+      acc = higher;
+      d = 4 * lane + 3;
+      const int bins[4] = {b0, b1, b2, b3};
+      for (int j = 3; j >= 0; --j) {
+        if (acc + bins[j] >= want) {
+          d = 4 * lane + j;
+          break;
+        }
+        acc += bins[j];
+      }
+    }
+    const uint64_t who = __builtin_amdgcn_ballot_w64(mine);
+    const int src = __builtin_ctzll(who);
+    d = __shfl(d, src);
+    acc = __shfl(acc, src);
+    want -= acc;
+    prefix |= (uint64_t)d << shift;
+    mask |= (uint64_t)255 << shift;
+    wave_fence();
+  }
+  // prefix is K*; `want` keys equal to it are kept, the smallest positions first
+  const int per = (n + 63) / 64;
+  const int b = min(lane * per, n), e = min(b + per, n);
+  int c = 0, eq = 0;
+  for (int u = b; u < e; ++u) {
+    const uint64_t k = key[u];
+    c += k > prefix ? 1 : 0;
+    eq += k == prefix ? 1 : 0;
+  }
+  // exclusive prefixes of the equal keys and of the kept keys over the lanes
+  int eq_incl = eq;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(eq_incl, off);
+    if (lane >= off) eq_incl += y;
+  }
+  int eq_before = eq_incl - eq;
+  const int kept = c + max(0, min(eq, want - eq_before));
+  int kept_incl = kept;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(kept_incl, off);
+    if (lane >= off) kept_incl += y;
+  }
+  int o = kept_incl - kept;
+  for (int u = b; u < e; ++u) {
+    const uint64_t k = key[u];
+    bool keep = k > prefix;
+    if (k == prefix) keep = eq_before++ < want;
+    if (keep) out[o++] = u;
+  }
+}
+
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ns_select_kernel(
-    const double* __restrict__ logits, const int32_t* __restrict__ flat,
-    const int32_t* __restrict__ kv_tab, int n_q, int n_flat, int n_kv, int n_ns,
-    int32_t* __restrict__ ns) {
-  // LDS sized by n_kv at launch (a few KB), so many workgroups share a CU
+    const double* __restrict__ qc, const double* __restrict__ kc, double scale,
+    const int32_t* __restrict__ flat, const int32_t* __restrict__ kv_tab, int n_q, int n_flat,
+    int n_kv, int n_ns, int32_t* __restrict__ ns) {
+  static_assert(G <= kThreads / 64, "one wave per row");
+  constexpr int kPer = D / 16;  // dims per lane
+  constexpr int kRows = 4;      // key rows per group in flight
+  constexpr int kGroups = kThreads / 16;
+  // LDS sized by n_kv at launch (a few KB at common lengths)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* key = reinterpret_cast<uint64_t*>(smem);                     // [n_kv]
-  uint8_t* flag = smem + sizeof(uint64_t) * n_kv;                        // [n_kv]
-  int32_t* counts = reinterpret_cast<int32_t*>(smem + ns_counts_offset(n_kv));  // [waves]
-  const int f = blockIdx.x;
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem);                           // [G][n_kv]
+  int32_t* tab_s = reinterpret_cast<int32_t*>(smem + ns_tab_offset(G, n_kv));  // [n_kv]
+  int32_t* hist = reinterpret_cast<int32_t*>(smem + ns_hist_offset(G, n_kv));  // [waves][256]
+  const int f0 = blockIdx.x * G;
+  const int rows = min(G, n_flat - f0);
   const int64_t bh = blockIdx.y;
   const int tid = threadIdx.x;
-  const int i = flat[bh * n_flat + f];
-  const double* row = logits + (bh * n_q + i) * (int64_t)n_q;
-  const int32_t* tab = kv_tab + bh * n_kv;
-  for (int u = tid; u < n_kv; u += kThreads) key[u] = order_key(row[tab[u]]);
-  __syncthreads();
-  for (int u = tid; u < n_kv; u += kThreads) {
-    const uint64_t ku = key[u];
-    int rank = 0;
-    for (int v = 0; v < n_kv; ++v) {
-      const uint64_t kv = key[v];
-      rank += (kv > ku || (kv == ku && v < u)) ? 1 : 0;
+  const int wave = tid >> 6;
+  const int sub = tid & 15;  // lane within the 16-lane group of one key row
+  const int grp = tid >> 4;
+  const double* kh = kc + bh * n_q * (int64_t)D;
+  for (int u = tid; u < n_kv; u += kThreads) tab_s[u] = kv_tab[bh * n_kv + u];
+  // this lane's dims of the workgroup's flat rows (a missing row repeats the
+  // first; its keys are never ranked)
+  double qv[G][kPer];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int i = flat[bh * n_flat + f0 + (g < rows ? g : 0)];
+    const f64x2_t* qrow = reinterpret_cast<const f64x2_t*>(qc + (bh * n_q + i) * (int64_t)D);
+#pragma unroll
+    for (int c = 0; c < kPer / 2; ++c) {
+      const f64x2_t t = qrow[sub * (kPer / 2) + c];
+      qv[g][2 * c] = t[0];
+      qv[g][2 * c + 1] = t[1];
     }
-    flag[u] = rank < n_ns ? 1 : 0;
   }
   __syncthreads();
-  compact(flag, n_kv, ns + (bh * n_flat + f) * (int64_t)n_ns, nullptr, counts);
+  // kRows key rows per group in flight (the loads are cache hits whose
+  // latency, not their bytes, bounds this loop)
+  for (int u0 = grp; u0 < n_kv; u0 += kRows * kGroups) {
+    f64x2_t kv[kRows][kPer / 2];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int u = min(u0 + r * kGroups, n_kv - 1);  // (a clamped row is not stored)
+      const f64x2_t* krow = reinterpret_cast<const f64x2_t*>(kh + tab_s[u] * (int64_t)D);
+#pragma unroll
+      for (int c = 0; c < kPer / 2; ++c) kv[r][c] = krow[sub * (kPer / 2) + c];
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int u = u0 + r * kGroups;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < kPer / 2; ++c) {
+          acc = fma(qv[g][2 * c], kv[r][c][0], acc);
+          acc = fma(qv[g][2 * c + 1], kv[r][c][1], acc);
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+        if (sub == 0 && u < n_kv) key[g * n_kv + u] = order_key(acc * scale);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < rows)
+    wave_top(key + wave * n_kv, n_kv, n_ns, hist + 256 * wave,
+             ns + (bh * n_flat + f0 + wave) * (int64_t)n_ns);
 }
 
 }  // namespace
 
-hipError_t launch_ns_select(const double* logits, const int32_t* flat, const int32_t* kv_tab,
-                            int BH, int n_q, int n_flat, int n_kv, int n_ns, int32_t* ns,
-                            hipStream_t stream) {
+hipError_t launch_ns_select(const double* qc, const double* kc, const int32_t* flat,
+                            const int32_t* kv_tab, int BH, int n_q, int D, int n_flat, int n_kv,
+                            int n_ns, int32_t* ns, hipStream_t stream) {
   if (BH == 0 || n_flat == 0 || n_ns == 0) return hipSuccess;
-  if (n_kv < 1 || n_kv > kMaxBlocksPerHead || n_ns > n_kv) return hipErrorInvalidValue;
-  const size_t lds = ns_counts_offset(n_kv) + sizeof(int32_t) * (kThreads / 64);
-  hipLaunchKernelGGL(ns_select_kernel, dim3(n_flat, BH), dim3(kThreads), lds, stream, logits,
-                     flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
+  if (n_kv < 1 || n_kv > kMaxBlocksPerHead || n_ns > n_kv || (D != 64 && D != 128))
+    return hipErrorInvalidValue;
+  const double scale = 1.0 / sqrt((double)D);
+  const bool four = ns_lds_bytes(4, n_kv) <= 65536;
+  const int G = four ? 4 : 1;
+  const size_t lds = ns_lds_bytes(G, n_kv);
+  const dim3 grid((n_flat + G - 1) / G, BH);
+  if (D == 128 && four)
+    hipLaunchKernelGGL((ns_select_kernel<128, 4>), grid, dim3(kThreads), lds, stream, qc, kc,
+                       scale, flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
+  else if (D == 128)
+    hipLaunchKernelGGL((ns_select_kernel<128, 1>), grid, dim3(kThreads), lds, stream, qc, kc,
+                       scale, flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
+  else if (four)
+    hipLaunchKernelGGL((ns_select_kernel<64, 4>), grid, dim3(kThreads), lds, stream, qc, kc,
+                       scale, flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
+  else
+    hipLaunchKernelGGL((ns_select_kernel<64, 1>), grid, dim3(kThreads), lds, stream, qc, kc,
+                       scale, flat, kv_tab, n_q, n_flat, n_kv, n_ns, ns);
   return hipGetLastError();
 }
 

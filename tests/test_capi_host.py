@@ -123,8 +123,10 @@ def test_plan_validation(kw, status):
 
 @pytest.mark.parametrize("alpha_ns", [0.0, 0.0625, 0.3, 1.0])
 def test_block_mask_count_and_workspace(alpha_ns):
-    # the count follows the oracle's rounding (R21); the mask adds the coarse
-    # logits and the per-block lists to the workspace only when it is used
+    # the count follows the oracle's rounding (R21); the mask adds only its
+    # per-block lists [B, H, n_flat, n_ns] to the workspace, and only when it
+    # is used: the coarse logits it ranks are recomputed per flat block, never
+    # stored as an [N_Q, N_Q] matrix
     base = isa.isa_plan_create(1, 3, 4096, 4096, 128, 64, 0.25, 0.5)
     p = isa.isa_plan_create(1, 3, 4096, 4096, 128, 64, 0.25, 0.5, alpha_ns)
     n_kv = p.info["n_kv_blocks"]
@@ -134,8 +136,18 @@ def test_block_mask_count_and_workspace(alpha_ns):
     if p.info["n_ns"] == 0:
         assert extra == 0
     else:
-        need = 3 * 128 * 128 * 8 + 3 * p.info["n_flat"] * p.info["n_ns"] * 4
-        assert need <= extra <= need + 512
+        need = 3 * p.info["n_flat"] * p.info["n_ns"] * 4
+        assert need <= extra <= need + 256
+
+
+def test_block_mask_workspace_does_not_grow_with_the_square_of_the_blocks():
+    # at the longest head (4096 blocks) an [N_Q, N_Q] fp64 matrix alone would
+    # be 128 MiB per head; the mask's lists are n_flat * n_ns * 4 bytes
+    for L in (16384, 131072):
+        base = isa.isa_plan_create(1, 1, L, L, 128, 64, 0.25, 0.5)
+        p = isa.isa_plan_create(1, 1, L, L, 128, 64, 0.25, 0.5, 0.0625)
+        lists = p.info["n_flat"] * p.info["n_ns"] * 4
+        assert p.info["workspace_bytes"] - base.info["workspace_bytes"] <= lists + 256
 
 
 @pytest.mark.parametrize("L_src,L_ctx", [(100, 200), (50, 0), (64, 1), (1000, 1000), (4097, 63)])

@@ -2,9 +2,8 @@
 
 A head of 4096 blocks is the longest a plan accepts (N = 262144 tokens at
 b = 64).  These cases run B*H = 5*13 = 65 such heads, so the last head of Q,
-K, V and O starts 64 * 2^25 = 2^31 elements (4 GiB of bf16) into its tensor
-and the block mask's stored coarse logits reach 8.7 GB: every per-head offset
-beyond 32 bits is exercised.  The heads repeat two drawn heads (head i holds
+K, V and O starts 64 * 2^25 = 2^31 elements (4 GiB of bf16) into its tensor:
+every per-head offset beyond 32 bits is exercised.  The heads repeat two drawn heads (head i holds
 the inputs of drawn head i mod 2), which keeps the host work to two heads.
 Every head must then reproduce its drawn head bit for bit (each step is
 deterministic and no step mixes heads), and the two drawn heads are checked
