@@ -235,25 +235,35 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   const float* lseh = p.lse + bh * p.lse_head_stride;
   const float* dlth = p.delta + bh * p.lse_head_stride;
   const int32_t* qtab = p.q_tab + bh * p.q_tab_stride;
-  // threads 0-255 stage Q, 256-511 stage dO (both layouts)
+  // threads 0-255 stage Q, 256-511 stage dO (both layouts).  Two register
+  // stages alternate, so a query block's loads are issued two iterations
+  // before its LDS copy is written (the LDS holds two blocks: no room for a
+  // third).
   const int half = tid >> 8;
-  Stager16<D> st;
-  st.init(tid & 255);
-  float st_lse = 0.0f;  // thread tid < 64: lse2 of query row tid; 64..127: delta
-  auto load = [&](int e) __attribute__((always_inline)) {
+  struct Stage {
+    Stager16<D> st;
+    float lse;  // thread tid < 64: lse of query row tid; 64..127: delta (as loaded)
+  };
+  Stage sa, sb;
+  sa.st.init(tid & 255);
+  sb.st.init(tid & 255);
+  sa.lse = sb.lse = 0.0f;
+  auto load = [&](Stage& x, int e) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)qtab[e] * kBlock;
     auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
-    st.load(half ? dOh : Qh, row_of);
-    if (tid < kBN)
-      st_lse = (lseh[r0 + tid] - p.lse_offset) * 1.4426950408889634f;
-    else if (tid < 2 * kBN)
-      st_lse = dlth[r0 + tid - kBN];
+    x.st.load(half ? dOh : Qh, row_of);
+    // Every thread issues one more load (threads past 127 discard theirs), and
+    // the value is converted only when stored: the same loads in every
+    // iteration, with no arithmetic on them here, let the wait before each
+    // store count exactly the newer stage's loads as still in flight.
+    x.lse = (tid & kBN ? dlth : lseh)[r0 + (tid & (kBN - 1))];
   };
-  auto store = [&](int buf) __attribute__((always_inline)) {
+  auto store = [&](Stage& x, int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
-    st.store(b + half * RS<D>::kBytes, b + 2 * RS<D>::kBytes + half * TS::bytes<D>());
+    x.st.store(b + half * RS<D>::kBytes, b + 2 * RS<D>::kBytes + half * TS::bytes<D>());
     if (tid < 2 * kBN)
-      reinterpret_cast<float*>(b + 2 * RS<D>::kBytes + 2 * TS::bytes<D>())[tid] = st_lse;
+      reinterpret_cast<float*>(b + 2 * RS<D>::kBytes + 2 * TS::bytes<D>())[tid] =
+          tid < kBN ? (x.lse - p.lse_offset) * 1.4426950408889634f : x.lse;
   };
 
   f32x4_t dk[ND], dv[ND];
@@ -267,13 +277,16 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   const float sl2 = p.scale_log2;
   const int n_q = p.n_q_entries;
   if (n_q > 0) {
-    load(0);
-    store(0);
+    load(sa, 0);
+    store(sa, 0);
+    load(sa, min(1, n_q - 1));
+    load(sb, min(2, n_q - 1));
   }
   __syncthreads();
-  for (int e = 0; e < n_q; ++e) {
+  // iteration e computes with query block e (LDS buffer e & 1), then writes
+  // block e + 1 from stage x into the other buffer and reloads x with e + 3
+  auto iteration = [&](int e, Stage& x) __attribute__((always_inline)) {
     const int buf = e & 1;
-    if (e + 1 < n_q) load(e + 1);
     const unsigned char* qt = smem + buf * kStage;
     const unsigned char* ot = qt + RS<D>::kBytes;
     const unsigned char* qtr = ot + RS<D>::kBytes;
@@ -328,9 +341,16 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
       const bf16x8_t b1 = ts_operand(qtr, 16 * j, 1, q, g);
       dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, ds1, dk[j], 0, 0, 0);
     }
-    if (e + 1 < n_q) store(buf ^ 1);
+    if (e + 1 < n_q) store(x, buf ^ 1);
+    load(x, min(e + 3, n_q - 1));  // (past the end: a block loaded again, unused)
     __syncthreads();
+  };
+  int e = 0;
+  for (; e + 1 < n_q; e += 2) {
+    iteration(e, sa);
+    iteration(e + 1, sb);
   }
+  if (e < n_q) iteration(e, sa);
   if (!key_valid) return;
 
   // lane (q, g): key q, dims 16 j + 4 g .. + 3
@@ -423,12 +443,15 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   const int32_t* tab = p.kv_tab + bh * p.kv_tab_stride;
   const int n_tiles = (p.kv_rows + kBN - 1) / kBN;
 
-  // threads 0-255 stage K (both layouts), 256-511 stage V (row-major)
+  // threads 0-255 stage K (both layouts), 256-511 stage V (row-major).  Two
+  // register stages alternate, so a key tile's loads are issued two
+  // iterations before its LDS copy is written.
   const int half = tid >> 8;
-  Stager16<D> st;
-  st.init(tid & 255);
+  Stager16<D> sa, sb;
+  sa.init(tid & 255);
+  sb.init(tid & 255);
   const bf16_bits* src = half ? Vh : Kh;
-  auto load = [&](int t) __attribute__((always_inline)) {
+  auto load = [&](Stager16<D>& st, int t) __attribute__((always_inline)) {
     if constexpr (kRowTable) {
       auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
         return tab[min(t * kBN + r, p.kv_rows - 1)];
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
       st.load(src, row_of);
     }
   };
-  auto store = [&](int buf) __attribute__((always_inline)) {
+  auto store = [&](Stager16<D>& st, int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
     st.store(b + half * RS<D>::kBytes, half ? nullptr : b + 2 * RS<D>::kBytes);
   };
@@ -452,12 +475,18 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i) dq[j][i] = 0.0f;
   const float sl2 = p.scale_log2;
 
-  load(0);
-  store(0);
+  load(sa, 0);
+  store(sa, 0);
+  // the same loads in every iteration (a tile past the end is the last one
+  // loaded again, unused), so the wait before each store counts exactly the
+  // newer stage's loads as still in flight
+  load(sa, min(1, n_tiles - 1));
+  load(sb, min(2, n_tiles - 1));
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
+  // iteration t computes with key tile t (LDS buffer t & 1), then writes tile
+  // t + 1 from stage x into the other buffer and reloads x with tile t + 3
+  auto iteration = [&](int t, Stager16<D>& x) __attribute__((always_inline)) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) load(t + 1);
     const unsigned char* kt = smem + buf * kStage;
     const unsigned char* vt = kt + RS<D>::kBytes;
     const unsigned char* ktr = vt + RS<D>::kBytes;
@@ -501,9 +530,16 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
       const bf16x8_t a1 = ts_operand(ktr, 16 * j, 1, q, g);
       dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ds1, dq[j], 0, 0, 0);
     }
-    if (t + 1 < n_tiles) store(buf ^ 1);
+    if (t + 1 < n_tiles) store(x, buf ^ 1);
+    load(x, min(t + 3, n_tiles - 1));
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    iteration(t, sa);
+    iteration(t + 1, sb);
   }
+  if (t < n_tiles) iteration(t, sa);
   if (!wave_valid) return;
   bf16_bits* dQh = p.dq + bh * p.q_head_stride + qrow * D;
   const float sc = p.inv_sqrt_d;
