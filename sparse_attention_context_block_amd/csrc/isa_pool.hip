@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
   constexpr int JMAX = (kBlock + RP - 1) / RP;  // rows per thread of a block (angle cache)
   // heads per workgroup: with the angle cache, one block's angles serve this many heads
   constexpr int kHeads = kCache ? kRopeHeads : 1;
-  __shared__ double red[3][RP][D];
+  // per-wave partial sums (the lanes of a wave are reduced with shuffles first)
+  __shared__ double red[3][kThreads / 64][D];
 
   const int blk = blockIdx.x;
   const int64_t bh0 = (int64_t)blockIdx.y * kHeads;
@@ -190,16 +191,35 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
       for (int j = 0; j < JMAX; ++j)
         if (r0 + RP * j < rows) process(r0 + RP * j, j, uq[j], uk[j], uv[j]);
     } else {
-      for (int r = r0; r < rows; r += RP) {
-        uint4 uq, uk, uv;
-        load(r, uq, uk, uv);
-        process(r, 0, uq, uk, uv);
+      // up to four passes' loads in flight before the first row is processed
+      // (rows past the end read the last row and are not processed)
+      constexpr int kAhead = 4;
+      for (int r = r0; r < rows; r += kAhead * RP) {
+        uint4 uq[kAhead], uk[kAhead], uv[kAhead];
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) load(min(r + RP * j, rows - 1), uq[j], uk[j], uv[j]);
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j)
+          if (r + RP * j < rows) process(r + RP * j, 0, uq[j], uk[j], uv[j]);
       }
     }
+    // Sum the row groups: first the lanes of a wave that hold the same dims
+    // (lane bits above the chunk index), then the four waves' sums in LDS.
+    // Block sums of bf16 (or fp32) values in fp64 are exact, so the order of
+    // the additions does not change them.
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+    for (int off = CH; off < 64; off <<= 1)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) red[t][r0][c * EPC + e] = acc[t][e];
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[t][e] += __shfl_xor(acc[t][e], off);
+    if (lane < CH) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) red[t][wave][c * EPC + e] = acc[t][e];
+    }
     __syncthreads();
 
     const int64_t out = (bh * n_q + blk) * (int64_t)D;
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
       const int t = idx / D, d = idx % D;
       double s = 0.0;
 #pragma unroll
-      for (int g = 0; g < RP; ++g) s += red[t][g][d];  // fixed order
+      for (int g = 0; g < kThreads / 64; ++g) s += red[t][g][d];
       const double mean = s / (double)rows;
       if (t == 0) {
         qc[out + d] = mean;
