@@ -571,8 +571,10 @@ def sweep(args):
     print(json.dumps(out), flush=True)
 
 
-def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_w64_kernel<1, false>"):
-    """Traffic file text: per-launch HBM bytes of `kernel`, from rocprofv3
+def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_w64_kernel<1, false>", grid=655360):
+    """Traffic file text: per-launch HBM bytes of `kernel` at `grid` threads
+    (the exact path at the 32K workload: 2560 workgroups x 256; the dense
+    baseline runs the same kernel at another grid), from rocprofv3
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on
     the 256 MiB copy of --calibrate-copy (268435456 bytes read and written)."""
     import csv
@@ -582,7 +584,7 @@ def hbm_traffic(fetch_csv, write_csv, kernel="attn_fwd_w64_kernel<1, false>"):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            if _short(r["Kernel_Name"]) == kernel:
+            if _short(r["Kernel_Name"]) == kernel and int(r["Grid_Size"]) == grid:
                 vals.append(float(r["Counter_Value"]))
             elif "MulFunctor" in r["Kernel_Name"]:
                 copy.append(float(r["Counter_Value"]))
