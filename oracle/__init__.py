@@ -57,4 +57,5 @@ from .isa_oracle_rope import (  # noqa: F401
     rotate_pairs,
     decoupled_rope,
     isa_ref_rope,
+    isa_ref_bwd_rope,
 )

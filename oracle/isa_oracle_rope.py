@@ -42,11 +42,14 @@ def round_to_bf16(x):
 
 
 def round_to_dtype(x, dtype):
-    """fp64 -> the values of the storage type ("bf16" or "fp32"), as fp64."""
+    """fp64 -> the values of the storage type ("bf16" or "fp32"), as fp64.
+    "fp64" stores unrounded (used by the finite-difference pins)."""
     if dtype == "bf16":
         return round_to_bf16(x)
     if dtype == "fp32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "fp64":
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(dtype)
 
 
@@ -97,6 +100,30 @@ def isa_ref_rope(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, rope_base, dtype, a
     out = isa_ref(Qr, Kr, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns)
     out["Qr"], out["Kr"] = Qr, Kr
     return out
+
+
+def isa_ref_bwd_rope(Q, K, V, dO, L_src, L_ctx, b, sel, flat, rope_base, dtype):
+    """Gradients (dQ, dK, dV) of sum(dO * O) of the ISA forward with the
+    decoupled RoPE (R24) and the decisions sel, flat fixed (R20).
+
+    The embedding turns each pair of Q and K by an angle that depends only on
+    the token's position: Q' = R Q with R orthogonal, so the chain rule gives
+    dQ = R^T dQ', each pair of dQ' turned back by the same angle, and likewise
+    for K; V is not rotated.  dQ', dK', dV are the backward of the rotated
+    forward (isa_ref_bwd at the rotated inputs).  The rounding of the rotated
+    values to the storage type (R24) is a storage step, not a part of the
+    function: the gradient is that of the rotation itself, evaluated at the
+    rounded Q', K' the forward used (as a layer stores its output and
+    back-propagates through its arithmetic)."""
+    from .isa_oracle_bwd import isa_ref_bwd
+
+    Q = np.asarray(Q, dtype=np.float64)
+    N, D = Q.shape[-2], Q.shape[-1]
+    Qr = decoupled_rope(Q, L_src, rope_base, dtype)
+    Kr = decoupled_rope(K, L_src, rope_base, dtype)
+    dQr, dKr, dV = isa_ref_bwd(Qr, Kr, V, dO, L_src, L_ctx, b, sel, flat)
+    theta = rope_positions(L_src, N - L_src)[:, None] * rope_inv_freq(D, rope_base)[None, :]
+    return rotate_pairs(dQr, -theta), rotate_pairs(dKr, -theta), dV
 
 
 def rope_angle(pos, i, D, base):

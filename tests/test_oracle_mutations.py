@@ -69,6 +69,12 @@ ROPE_MUTATIONS = [
      ".astype(np.float64))"),
     ("bf16 rounding ties away from zero", "return np.ldexp(np.rint(m * 256.0), e - 8)",
      "return np.ldexp(np.trunc(m * 256.0 + np.copysign(0.5, m)), e - 8)"),
+    ("rope backward turns the gradient forward, not back",
+     "return rotate_pairs(dQr, -theta), rotate_pairs(dKr, -theta), dV",
+     "return rotate_pairs(dQr, theta), rotate_pairs(dKr, theta), dV"),
+    ("rope backward leaves dK unturned",
+     "return rotate_pairs(dQr, -theta), rotate_pairs(dKr, -theta), dV",
+     "return rotate_pairs(dQr, -theta), dKr, dV"),
 ]
 
 ALL = [(n, o, w, "isa_oracle.py") for n, o, w in MUTATIONS] + \

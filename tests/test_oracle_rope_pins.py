@@ -139,3 +139,45 @@ def test_isa_with_rope_is_isa_on_the_rotated_inputs():
     # the rotation changes the result (it is not silently skipped)
     plain = orc.isa_ref(Q, K, V, 256, 192, 64, 0.5, 0.5)
     assert np.abs(plain["O"] - out["O"]).max() > 1e-3
+
+
+def test_rope_backward_finite_differences():
+    """The decision-frozen backward with the rotary embedding (R20 with R24)
+    against central finite differences of the forward it differentiates: the
+    rotated inputs stored unrounded ("fp64"), the decisions fixed from the
+    rotated inputs.  A wrong direction of the turn back (R instead of R^T) or
+    a missing turn fails at every non-zero angle; position 0 of each segment
+    (angle 0) is the only place the two agree."""
+    rng = np.random.default_rng(41)
+    L_src, L_ctx, b, D, base = 8, 12, 4, 4, 50.0
+    N = L_src + L_ctx
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, D)) for _ in range(4))
+    Qr = orc.decoupled_rope(Q, L_src, base, "fp64")
+    Kr = orc.decoupled_rope(K, L_src, base, "fp64")
+    d = orc.decisions_ref(Qr, Kr, L_src, L_ctx, b, 0.5, 0.5)
+    assert len(d["flat"][0, 0]) > 0 and len(d["sharp"][0, 0]) > 0
+    sel, flat = d["sel"], d["flat"]
+    dQ, dK, dV = orc.isa_ref_bwd_rope(Q, K, V, dO, L_src, L_ctx, b, sel, flat, base, "fp64")
+
+    def loss():
+        O, _ = orc.isa_ref_fixed(orc.decoupled_rope(Q, L_src, base, "fp64"),
+                                 orc.decoupled_rope(K, L_src, base, "fp64"), V,
+                                 L_src, L_ctx, b, sel, flat)
+        return float((O * dO).sum())
+
+    eps = 1e-6
+    for X, G in ((Q, dQ), (K, dK), (V, dV)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            old = X[idx]
+            X[idx] = old + eps
+            lp = loss()
+            X[idx] = old - eps
+            lm = loss()
+            X[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        scale = np.abs(num).max()
+        np.testing.assert_allclose(G, num, atol=1e-6 * scale, rtol=0)
+    # the turn back matters: the unrotated gradient of the rotated forward differs
+    dQr, _, _ = orc.isa_ref_bwd(Qr, Kr, V, dO, L_src, L_ctx, b, sel, flat)
+    assert np.abs(dQr - dQ).max() > 1e-3 * np.abs(dQ).max()
