@@ -226,10 +226,15 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * they must be what isa_forward wrote for this plan (sel: k distinct ascending
  * context block ids; flat and sharp: together every query block once, each
  * list ascending), or the kernels read and write outside the tensors.
- * workspace: at least isa_backward_workspace_bytes().
+ * With rope_base > 0 the gradient is taken at the rotated Q and K the forward
+ * used (re-rotated into the workspace, bit for bit the forward's), and dQ, dK
+ * are turned back by each token's angle (the rotation is orthogonal per pair,
+ * so dQ = R^T dQ'); the rounding of the rotated values is a storage step.
+ * workspace: at least isa_backward_workspace_bytes() (with rope_base > 0 it
+ * holds the rotated Q and K, two [B, H, N, D] copies).
  * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, block != 64, a
- * plan with n_ns > 0 or rope_base > 0, or L_src / L_ctx not a multiple of
- * 64), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
+ * plan with n_ns > 0 and flat blocks, or L_src / L_ctx not a multiple of 64),
+ * ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

@@ -524,7 +524,9 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
 namespace {
 
 struct BwdLayout {
-  size_t delta, kv_tab, iota, kc, vc, dkc, dvc, total;
+  size_t delta, kv_tab, iota, kc, vc, dkc, dvc;
+  size_t qr, kr;  // rotary embedding only: the rotated Q and K
+  size_t total;
 };
 
 BwdLayout bwd_layout(const isa_plan_s* p) {
@@ -543,6 +545,9 @@ BwdLayout bwd_layout(const isa_plan_s* p) {
   w.vc = take(BH * n_kv * D * 2);
   w.dkc = take(BH * n_kv * D * sizeof(float));
   w.dvc = take(BH * n_kv * D * sizeof(float));
+  const size_t tokens = BH * (size_t)p->N * D * elt_size(p->d.dtype);
+  w.qr = p->rope ? take(tokens) : 0;
+  w.kr = p->rope ? take(tokens) : 0;
   w.total = off;
   return w;
 }
@@ -572,7 +577,6 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
   if (plan->info.n_ns > 0 && plan->info.n_flat > 0) return ISA_ERR_UNSUPPORTED;
   if (!plan->aligned || plan->d.block != kBlock) return ISA_ERR_UNSUPPORTED;
-  if (plan->rope) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);
@@ -586,6 +590,18 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   L.k = (int)in.k;
   L.n_flat = (int)in.n_flat;
   L.n_sharp = (int)in.n_sharp;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int N = (int)plan->N, D = plan->d.D;
+  if (plan->rope) {
+    // the forward saw the rotated Q and K: rotate them again (bit-identical to
+    // the forward's copies), differentiate at them, and turn dQ, dK back below
+    ISA_LAUNCH(launch_rope_rotate(Q, w + W.qr, plan->d.dtype, plan->BH, N, D, plan->d.L_src,
+                                  plan->freq, false, s));
+    ISA_LAUNCH(launch_rope_rotate(K, w + W.kr, plan->d.dtype, plan->BH, N, D, plan->d.L_src,
+                                  plan->freq, false, s));
+    Q = w + W.qr;
+    K = w + W.kr;
+  }
   L.Q = static_cast<const bf16_bits*>(Q);
   L.K = static_cast<const bf16_bits*>(K);
   L.V = static_cast<const bf16_bits*>(V);
@@ -605,7 +621,14 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   L.vc = reinterpret_cast<bf16_bits*>(w + W.vc);
   L.dkc = reinterpret_cast<float*>(w + W.dkc);
   L.dvc = reinterpret_cast<float*>(w + W.dvc);
-  ISA_LAUNCH(launch_backward(L, static_cast<hipStream_t>(stream)));
+  ISA_LAUNCH(launch_backward(L, s));
+  if (plan->rope) {
+    // dQ = R^T dQ', dK = R^T dK' (each pair turned back by its angle)
+    ISA_LAUNCH(launch_rope_rotate(dQ, dQ, plan->d.dtype, plan->BH, N, D, plan->d.L_src,
+                                  plan->freq, true, s));
+    ISA_LAUNCH(launch_rope_rotate(dK, dK, plan->d.dtype, plan->BH, N, D, plan->d.L_src,
+                                  plan->freq, true, s));
+  }
   return ISA_OK;
 }
 

@@ -202,6 +202,12 @@ hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t 
                        double* qc, double* kc, void* kc_lp, void* vc_lp, void* qr, void* kr,
                        const RopeFreq* rope, hipStream_t stream);
 
+// Every pair of X turned by its rotary angle (inverse: turned back), rounded
+// once to the storage type, into Y (may be X).  The forward direction equals
+// the pooling kernel's rotation bit for bit.
+hipError_t launch_rope_rotate(const void* X, void* Y, isa_dtype_t dtype, int BH, int N, int D,
+                              int L_src, const RopeFreq& rope, bool inverse, hipStream_t stream);
+
 hipError_t launch_coarse_rowstats(const double* qc, const double* kc, int BH, int n_q, int D,
                                   double* rowmax, double* rowsum, double* sharpness,
                                   hipStream_t stream);

@@ -242,6 +242,39 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
   }
 }
 
+// Rotation alone, for the backward with the rotary embedding: Y = X with
+// every pair turned by its angle (sign = +1: the forward's rotation, the same
+// arithmetic and single rounding as the pooling kernel, so Y equals the
+// rotated copy the forward used bit for bit) or turned back (sign = -1: the
+// gradient of the rotation, dX = R^T dY).  One thread per (token, 16-byte
+// chunk), looping over the heads, so each angle's sine and cosine are computed
+// once for all heads.  In place (Y == X) is allowed.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void rope_rotate_kernel(const T* X, T* Y, int BH, int N,
+                                                               int L_src, RopeFreq rope,
+                                                               double sign) {
+  constexpr int EPC = Elt<T>::kPerChunk;
+  constexpr int CH = D / EPC;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= (int64_t)N * CH) return;
+  const int t = (int)(gid / CH), c = (int)(gid % CH);
+  const double pos = (double)(t < L_src ? t : t - L_src);
+  double cs[EPC / 2], sn[EPC / 2];
+#pragma unroll
+  for (int pr = 0; pr < EPC / 2; ++pr) {
+    sincos(pos * rope.inv_freq[c * (EPC / 2) + pr], &sn[pr], &cs[pr]);
+    sn[pr] *= sign;
+  }
+  for (int bh = 0; bh < BH; ++bh) {
+    const int64_t off = ((int64_t)bh * N + t) * D + c * EPC;
+    double x[EPC];
+    Elt<T>::unpack(*reinterpret_cast<const uint4*>(X + off), x);
+#pragma unroll
+    for (int pr = 0; pr < EPC / 2; ++pr) rotate_pair(x[2 * pr], x[2 * pr + 1], cs[pr], sn[pr]);
+    *reinterpret_cast<uint4*>(Y + off) = Elt<T>::round_pack(x);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const void* Q, const void* K, const void* V, int BH, int N,
                         int L_src, int n_src, int n_q, int block, double* qc, double* kc,
@@ -273,6 +306,34 @@ hipError_t launch_typed(const void* Q, const void* K, const void* V, int BH, int
 }
 
 }  // namespace
+
+hipError_t launch_rope_rotate(const void* X, void* Y, isa_dtype_t dtype, int BH, int N, int D,
+                              int L_src, const RopeFreq& rope, bool inverse, hipStream_t stream) {
+  if (BH == 0 || N == 0) return hipSuccess;
+  const double sign = inverse ? -1.0 : 1.0;
+  const int64_t chunks = (int64_t)N * (D * (dtype == ISA_DTYPE_BF16 ? 2 : 4) / 16);
+  const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
+  if (dtype == ISA_DTYPE_BF16) {
+    if (D == 128)
+      hipLaunchKernelGGL((rope_rotate_kernel<bf16_bits, 128>), grid, dim3(kThreads), 0, stream,
+                         static_cast<const bf16_bits*>(X), static_cast<bf16_bits*>(Y), BH, N,
+                         L_src, rope, sign);
+    else
+      hipLaunchKernelGGL((rope_rotate_kernel<bf16_bits, 64>), grid, dim3(kThreads), 0, stream,
+                         static_cast<const bf16_bits*>(X), static_cast<bf16_bits*>(Y), BH, N,
+                         L_src, rope, sign);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((rope_rotate_kernel<float, 128>), grid, dim3(kThreads), 0, stream,
+                         static_cast<const float*>(X), static_cast<float*>(Y), BH, N, L_src,
+                         rope, sign);
+    else
+      hipLaunchKernelGGL((rope_rotate_kernel<float, 64>), grid, dim3(kThreads), 0, stream,
+                         static_cast<const float*>(X), static_cast<float*>(Y), BH, N, L_src,
+                         rope, sign);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_pool(const void* Q, const void* K, const void* V, isa_dtype_t dtype, int BH,
                        int N, int D, int L_src, int n_src, int n_q, int block, double* qc,

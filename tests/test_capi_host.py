@@ -200,15 +200,22 @@ def test_rope_workspace_holds_the_rotated_q_and_k():
         {k: v for k, v in plain.info.items() if k != "workspace_bytes"}
 
 
-def test_backward_with_rope_unsupported():
+def test_backward_with_rope_takes_the_rotated_copies_in_its_workspace():
+    # the backward re-rotates Q and K into its workspace (two [B, H, N, D]
+    # copies) and turns dQ, dK back; the check of the workspace size comes
+    # before any launch
     lib = isa._lib()
+    base = isa.isa_plan_create(1, 2, 256, 256, 128, 64, 0.5, 0.5)
     p = isa.isa_plan_create(1, 2, 256, 256, 128, 64, 0.5, 0.5, rope_base=10000.0)
+    need = lib.isa_backward_workspace_bytes(p.handle)
+    extra = need - lib.isa_backward_workspace_bytes(base.handle)
+    assert 2 * 2 * 512 * 128 * 2 <= extra <= 2 * 2 * 512 * 128 * 2 + 512
     fake = ctypes.c_void_p(0x1000)
     a = isa.isa_aux_t()
     a.sel = a.flat = a.sharp = 0x1000
     st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
-                          fake, fake, fake, fake, 1 << 40, None)
-    assert st == isa.ISA_ERR_UNSUPPORTED
+                          fake, fake, fake, fake, need - 16, None)
+    assert st == isa.ISA_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("block,L_src,L_ctx", [(32, 500, 300), (128, 1000, 700), (32, 512, 384),
