@@ -144,6 +144,15 @@ __device__ __forceinline__ void anchor(float x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// max of two finite scores or -inf: a plain v_max_f32 (fmaxf would first
+// canonicalize each operand that does not come from arithmetic, here the
+// outputs of a lane swap, with two more instructions)
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // kShift: log2 of the 32-row slices per block, 1 (b = 64) or 2 (b = 128).
 // kPartial: some key tiles may hold fewer than 64 valid rows (plans whose
 // source or context length is not a multiple of b); without it every tile is
@@ -370,6 +379,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     const int c = pr >> 3, h = (pr >> 2) & 1, e2 = 2 * (pr & 3);
     pk[h][c][e2] = (__bf16)pe[pr & 1][0];
     pk[h][c][e2 + 1] = (__bf16)pe[pr & 1][1];
+    // (the packed pair is used only by the next tile's products: without the
+    // anchor the compiler sinks the conversion out of its slot, to the start
+    // of the next iteration, where no product is in flight to hide it)
+    anchor(__uint_as_float(__builtin_bit_cast(u32x4, pk[h][c])[pr & 3]));
     l_run[h] = (l_run[h] + pe[pr & 1][0]) + pe[pr & 1][1];
     anchor(l_run[h]);
   };
@@ -450,9 +463,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
   //                    the previous tile's odd slots 49-63, after their last
   //                    product in slot 47)
   //   slots 16-21   running max and rescale decision, a dependent chain: swap
-  //                 with the partner lane; compare and ballot; new max; 2^(old -
-  //                 new); and, after tile t-1's last pair and before tile t's
-  //                 first, l *= alpha (slot 21)
+  //                 with the partner lane, one half per slot; compare and
+  //                 ballot; new max; 2^(old - new); and, after tile t-1's last
+  //                 pair and before tile t's first, l *= alpha (slot 21)
   //   odd slots 21-39  loads of tile t + 3, one per slot (into the ring slots
   //                 of K(t) and V(t-2), which no wave reads after the last barrier)
   // Fragment reads run three fragments (six slots) ahead of their products.
@@ -494,33 +507,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
       if constexpr (slot < 20) elem(Q, slot + 44);                          // tile t-1
       if constexpr (slot >= 20) elem(P, slot - 20);                         // tile t
       if constexpr (slot >= 1 && slot <= 15 && (slot & 1) == 1) max_step(P, 1, (slot - 1) >> 1);
-      if constexpr (slot == 16) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // the swap returns {own, partner} in an order that depends on the
-          // half of the wave, so take both
-          const uint32_t u = __float_as_uint(tmax[h]);
-          const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-          ts[h] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
-          anchor(ts[h]);
-        }
+      // running max and rescale decision, spread over slots 16-21: the swap
+      // with the partner lane and the tile max of half 0 (16) and half 1 (17),
+      // the ballots (18), the new max (19), 2^(old - new) (20) and l *= alpha
+      // (21, after tile t-1's last pair and before tile t's first)
+      if constexpr (slot == 16 || slot == 17) {
+        constexpr int h = slot - 16;
+        // the swap returns {own, partner} in an order that depends on the
+        // half of the wave, so take both
+        const uint32_t u = __float_as_uint(tmax[h]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        ts[h] = max2(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+        anchor(ts[h]);
       }
-      if constexpr (slot == 17) {
+      if constexpr (slot == 18) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           up[h] = __builtin_amdgcn_ballot_w64(ts[h] > m_run[h] + kRescaleThreshold) != 0;
       }
-      if constexpr (slot == 18) {
+      if constexpr (slot == 19) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float m_new = up[h] ? fmaxf(m_run[h], ts[h]) : m_run[h];
+          const float mx = max2(m_run[h], ts[h]);  // (unconditional: no branch)
+          const float m_new = up[h] ? mx : m_run[h];
           dm[h] = m_run[h] - m_new;
           m_run[h] = m_new;
           mneg[P][h] = -m_new;
           anchor(dm[h]);
+          anchor(mneg[P][h]);
         }
       }
-      if constexpr (slot == 19) {
+      if constexpr (slot == 20) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           alpha[h] = up[h] ? __builtin_amdgcn_exp2f(dm[h]) : 1.0f;
