@@ -14,6 +14,13 @@ passes through S_coarse.  The gradient flows through
     O_r = sum_j pi_rj V^c_j, plus the mean pooling K^c_j = (1/w_j) sum_{t in B_j} K_t
     (and V^c_j likewise), so dK_t += dK^c_j / w_j for every token t of block j.
 
+With the block mask inside flat rows (reading R21: the tokens of the blocks
+ns[f] of flat block f enter one by one, every other kept block through its
+representative with weight w_j, one softmax over both), a flat row's terms are
+the union of the two kinds above, so its gradient splits the same way: token
+terms feed dK_new, dV_new at those tokens, representative terms feed dK^c,
+dV^c.
+
 Rows of context blocks that were not selected receive zero gradient in K and V.
 """
 
@@ -31,7 +38,35 @@ def _softmax_bwd(P, dO, O, Vmat):
     return P * (dP - delta)
 
 
-def _head_bwd(Qh, Kh, Vh, dOh, L_src, L_ctx, b, sel, flat):
+def _mixed_rows_bwd(q, dO, K_new, V_new, Kc_new, Vc_new, w_new, exact_blocks, scale):
+    """Backward of one flat block's rows under the block mask: the columns are
+    the tokens of the K_new blocks in ``exact_blocks`` (weight 1) followed by
+    the representatives of the other kept blocks (weight w_j), one softmax.
+    Returns (dq, token positions, dK_tok, dV_tok, rep positions, dKc_rep, dVc_rep)."""
+    ends = np.cumsum(w_new).astype(np.int64)
+    starts = ends - w_new.astype(np.int64)
+    exact = np.zeros(len(w_new), dtype=bool)
+    exact[np.asarray(exact_blocks, dtype=np.int64)] = True
+    tok = (np.concatenate([np.arange(starts[u], ends[u]) for u in np.nonzero(exact)[0]])
+           if exact.any() else np.zeros(0, dtype=np.int64))
+    rep = np.nonzero(~exact)[0]
+    Kcols = np.concatenate([K_new[tok], Kc_new[rep]])
+    Vcols = np.concatenate([V_new[tok], Vc_new[rep]])
+    logw = np.concatenate([np.zeros(len(tok)), np.log(w_new[rep])])
+    S = (q @ Kcols.T) * scale + logw[None, :]
+    S -= S.max(axis=1, keepdims=True)
+    P = np.exp(S)
+    P /= P.sum(axis=1, keepdims=True)
+    O = P @ Vcols
+    dS = _softmax_bwd(P, dO, O, Vcols)
+    dq = (dS @ Kcols) * scale
+    dKcols = (dS.T @ q) * scale
+    dVcols = P.T @ dO
+    n = len(tok)
+    return dq, tok, dKcols[:n], dVcols[:n], rep, dKcols[n:], dVcols[n:]
+
+
+def _head_bwd(Qh, Kh, Vh, dOh, L_src, L_ctx, b, sel, flat, ns=None):
     starts, ends, n_src, n_ctx = block_grid(L_src, L_ctx, b)
     n_q = len(starts)
     N, D = Qh.shape
@@ -72,8 +107,19 @@ def _head_bwd(Qh, Kh, Vh, dOh, L_src, L_ctx, b, sel, flat):
         dQ[sharp_rows] = (dS @ K_new) * scale
         dK_new += (dS.T @ q) * scale
 
+    # flat rows under the block mask (R21): one mixed softmax per flat block
+    if len(flat_rows) and ns is not None and np.asarray(ns).size > 0:
+        for f, i in enumerate(np.asarray(flat, dtype=np.int64)):
+            rows = np.arange(starts[i], ends[i])
+            dq, tok, dkt, dvt, rep, dkr, dvr = _mixed_rows_bwd(
+                Qh[rows], dOh[rows], K_new, V_new, Kc_new, Vc_new, w_new, ns[f], scale)
+            dQ[rows] = dq
+            dK_new[tok] += dkt
+            dV_new[tok] += dvt
+            dKc[rep] += dkr
+            dVc[rep] += dvr
     # Taylor path (flat rows)
-    if len(flat_rows):
+    elif len(flat_rows):
         q = Qh[flat_rows]
         S = (q @ Kc_new.T) * scale
         S -= S.max(axis=1, keepdims=True)
@@ -97,10 +143,11 @@ def _head_bwd(Qh, Kh, Vh, dOh, L_src, L_ctx, b, sel, flat):
     return dQ, dK, dV
 
 
-def isa_ref_bwd(Q, K, V, dO, L_src, L_ctx, b, sel, flat):
+def isa_ref_bwd(Q, K, V, dO, L_src, L_ctx, b, sel, flat, ns=None):
     """Gradients (dQ, dK, dV) of sum(dO * O) with the decisions sel, flat fixed.
 
-    sel [B, H, k] and flat [B, H, n_flat] as returned by ``decisions_ref``.
+    sel [B, H, k] and flat [B, H, n_flat] as returned by ``decisions_ref``;
+    ns [B, H, n_flat, n_ns] (optional): the block mask of the flat blocks.
     """
     Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
     B, H = Q.shape[:2]
@@ -109,7 +156,7 @@ def isa_ref_bwd(Q, K, V, dO, L_src, L_ctx, b, sel, flat):
         for h in range(H):
             dQ[bi, h], dK[bi, h], dV[bi, h] = _head_bwd(
                 Q[bi, h], K[bi, h], V[bi, h], dO[bi, h], L_src, L_ctx, b,
-                sel[bi][h], flat[bi][h])
+                sel[bi][h], flat[bi][h], None if ns is None else ns[bi][h])
     return dQ, dK, dV
 
 

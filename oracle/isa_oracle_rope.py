@@ -102,7 +102,7 @@ def isa_ref_rope(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, rope_base, dtype, a
     return out
 
 
-def isa_ref_bwd_rope(Q, K, V, dO, L_src, L_ctx, b, sel, flat, rope_base, dtype):
+def isa_ref_bwd_rope(Q, K, V, dO, L_src, L_ctx, b, sel, flat, rope_base, dtype, ns=None):
     """Gradients (dQ, dK, dV) of sum(dO * O) of the ISA forward with the
     decoupled RoPE (R24) and the decisions sel, flat fixed (R20).
 
@@ -121,7 +121,7 @@ def isa_ref_bwd_rope(Q, K, V, dO, L_src, L_ctx, b, sel, flat, rope_base, dtype):
     N, D = Q.shape[-2], Q.shape[-1]
     Qr = decoupled_rope(Q, L_src, rope_base, dtype)
     Kr = decoupled_rope(K, L_src, rope_base, dtype)
-    dQr, dKr, dV = isa_ref_bwd(Qr, Kr, V, dO, L_src, L_ctx, b, sel, flat)
+    dQr, dKr, dV = isa_ref_bwd(Qr, Kr, V, dO, L_src, L_ctx, b, sel, flat, ns)
     theta = rope_positions(L_src, N - L_src)[:, None] * rope_inv_freq(D, rope_base)[None, :]
     return rotate_pairs(dQr, -theta), rotate_pairs(dKr, -theta), dV
 

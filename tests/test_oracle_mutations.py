@@ -53,6 +53,17 @@ MUTATIONS = [
      "E_rep = np.exp(S_rep - m)"),
 ]
 
+# mistakes in the backward (oracle/isa_oracle_bwd.py)
+BWD_MUTATIONS = [
+    ("Taylor backward drops the block weight", "Pi = np.exp(S) * w_new[None, :]",
+     "Pi = np.exp(S)"),
+    ("masked backward drops the representative weight",
+     "logw = np.concatenate([np.zeros(len(tok)), np.log(w_new[rep])])",
+     "logw = np.zeros(len(tok) + len(rep))"),
+    ("masked backward keeps only the last flat block's pooled gradient",
+     "            dKc[rep] += dkr\n", "            dKc[rep] = dkr\n"),
+]
+
 
 # mistakes in the rotary embedding (oracle/isa_oracle_rope.py)
 ROPE_MUTATIONS = [
@@ -78,7 +89,8 @@ ROPE_MUTATIONS = [
 ]
 
 ALL = [(n, o, w, "isa_oracle.py") for n, o, w in MUTATIONS] + \
-      [(n, o, w, "isa_oracle_rope.py") for n, o, w in ROPE_MUTATIONS]
+      [(n, o, w, "isa_oracle_rope.py") for n, o, w in ROPE_MUTATIONS] + \
+      [(n, o, w, "isa_oracle_bwd.py") for n, o, w in BWD_MUTATIONS]
 
 
 @pytest.mark.parametrize("name,old,new,fname", ALL, ids=[m[0] for m in ALL])
