@@ -15,7 +15,7 @@ input, and the fp64 CPU oracle timed on a bounded sample.  Extra sections time
 the same workload with the block mask inside flat query blocks (alpha_ns,
 default 0.0625), with the decoupled rotary embedding (base 10000) and with
 block lengths 32 and 128, and the decision-frozen backward of the B=2 N=16384
-workload.
+workload (also with the block mask at alpha_ns 0.0625).
 """
 
 import argparse
@@ -290,21 +290,24 @@ def bench_backward(args, isa, torch, dev):
     to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v, do = (to_gpu(inp[x]) for x in ("q", "k", "v", "do"))
     del inp
+    def time_bwd(plan):
+        o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
+        ws = torch.empty(max(isa._lib().isa_backward_workspace_bytes(plan.handle), 1),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            isa.isa_backward(plan, q, k, v, o, do, lse, aux, workspace=ws)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.bwd_steps):
+            isa.isa_backward(plan, q, k, v, o, do, lse, aux, workspace=ws)
+        s1.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / args.bwd_steps, o, lse
+
     plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"])
     info = plan.info
-    o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
-    ws = torch.empty(max(isa._lib().isa_backward_workspace_bytes(plan.handle), 1),
-                     dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        isa.isa_backward(plan, q, k, v, o, do, lse, aux, workspace=ws)
-    torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(args.bwd_steps):
-        isa.isa_backward(plan, q, k, v, o, do, lse, aux, workspace=ws)
-    s1.record()
-    torch.cuda.synchronize()
-    bms = s0.elapsed_time(s1) / args.bwd_steps
+    bms, o, lse = time_bwd(plan)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record()
     for _ in range(args.bwd_steps):
@@ -317,12 +320,23 @@ def bench_backward(args, isa, torch, dev):
     taylor_pairs = B * H * info["n_flat"] * b * info["n_kv_blocks"]
     bwd_flops = 10.0 * D * (exact_pairs + taylor_pairs)
     _log(f"backward {bms:.3f} ms, forward {fms:.3f} ms")
+    # the same workload with the block mask at the pages' ratio alpha_ns = 0.0625:
+    # each flat row takes n_ns blocks token by token, the rest as representatives
+    mplan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, c["alpha_s"], c["alpha_f"], 0.0625)
+    mi = mplan.info
+    mms, _, _ = time_bwd(mplan)
+    m_pairs = exact_pairs + B * H * mi["n_flat"] * b * (mi["n_ns"] * b + mi["n_kv_blocks"] - mi["n_ns"])
+    m_flops = 10.0 * D * m_pairs
+    _log(f"backward with the block mask (alpha_ns 0.0625, n_ns {mi['n_ns']}) {mms:.3f} ms")
     return {"workload": c["name"], "B": B, "H": H, "N": N, "alpha_s": c["alpha_s"],
             "alpha_f": c["alpha_f"], "fwd_ms": fms, "bwd_ms": bms,
             "bwd_algorithmic_tflop": bwd_flops / 1e12,
             "bwd_tflops": bwd_flops / (bms * 1e-3) / 1e12,
             "bwd_mfma_frac": bwd_flops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12}
+            "dense_equiv_fwd_bwd_tflops": 3.5 * 4.0 * B * H * N * N * D / ((fms + bms) * 1e-3) / 1e12,
+            "block_mask": {"alpha_ns": 0.0625, "n_ns": mi["n_ns"], "bwd_ms": mms,
+                           "bwd_algorithmic_tflop": m_flops / 1e12,
+                           "bwd_mfma_frac": m_flops / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
 
 
 def _fp64_rate(ms, flops):

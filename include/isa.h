@@ -230,11 +230,18 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * used (re-rotated into the workspace, bit for bit the forward's), and dQ, dK
  * are turned back by each token's angle (the rotation is orthogonal per pair,
  * so dQ = R^T dQ'); the rounding of the rotated values is a storage step.
+ * With the block mask (n_ns > 0 and flat blocks; [notes] key design 2: a
+ * block pair with mask 1 takes the exact update, otherwise the representative
+ * one) aux->ns is required too (n_ns distinct ascending positions in
+ * [0, n_kv) per flat block): a flat row's token terms of its exact blocks
+ * feed dK, dV of those tokens, its representative terms feed the pooled
+ * gradient of the other blocks.
  * workspace: at least isa_backward_workspace_bytes() (with rope_base > 0 it
- * holds the rotated Q and K, two [B, H, N, D] copies).
- * Errors: ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED (FP32, block != 64, a
- * plan with n_ns > 0 and flat blocks, or L_src / L_ctx not a multiple of 64),
- * ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
+ * holds the rotated Q and K, two [B, H, N, D] copies; with the block mask,
+ * the exact-block tables: about B * H * n_flat * (n_ns + n_kv / 32) * 4 bytes).
+ * Errors: ISA_ERR_INVALID_ARG (also a null aux->ns with the block mask),
+ * ISA_ERR_UNSUPPORTED (FP32, block != 64, or L_src / L_ctx not a multiple of
+ * 64), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

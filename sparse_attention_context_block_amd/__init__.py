@@ -302,27 +302,30 @@ def isa_dense_forward(q, k, v, o=None, lse=None, stream=None):
 
 
 def _decision_aux(plan, aux):
-    """isa_aux_t with the forward's decisions sel, flat, sharp for the backward.
+    """isa_aux_t with the forward's decisions sel, flat, sharp (and, with the
+    block mask, ns) for the backward.
 
     The backward kernels read these ids unchecked, so each must be an int32,
     contiguous [B, H, count] tensor of this plan (ValueError otherwise) on the
     GPU (TypeError otherwise)."""
     d, info = plan.desc, plan.info
     a = isa_aux_t()
-    counts = {"sel": info["k"], "flat": info["n_flat"], "sharp": info["n_sharp"]}
-    for f, n in counts.items():
+    shapes = {"sel": (d.B, d.H, info["k"]), "flat": (d.B, d.H, info["n_flat"]),
+              "sharp": (d.B, d.H, info["n_sharp"])}
+    if info["n_ns"] > 0 and info["n_flat"] > 0:  # the block mask of the flat blocks
+        shapes["ns"] = (d.B, d.H, info["n_flat"], info["n_ns"])
+    for f, shape in shapes.items():
         if f not in aux:
             raise ValueError(f"aux lacks {f!r}")
         t = aux[f]
-        shape = (d.B, d.H, n)
         if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 \
                 or tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"aux[{f!r}]: expected contiguous int32 {shape}, got "
                              f"{getattr(t, 'dtype', type(t))} {tuple(getattr(t, 'shape', ()))}")
-    for f, n in counts.items():
+    for f, shape in shapes.items():
         if not aux[f].is_cuda:
             raise TypeError(f"aux[{f!r}] must be a GPU tensor")
-        setattr(a, f, aux[f].data_ptr() if n else None)
+        setattr(a, f, aux[f].data_ptr() if shape[-1] else None)
     return a
 
 

@@ -526,6 +526,8 @@ namespace {
 struct BwdLayout {
   size_t delta, kv_tab, iota, kc, vc, dkc, dvc;
   size_t qr, kr;  // rotary embedding only: the rotated Q and K
+  // block mask only: exact-block tables of the flat blocks
+  size_t ns_mask, tok_list, tok_cnt, fq_off, fq_list;
   size_t total;
 };
 
@@ -548,6 +550,14 @@ BwdLayout bwd_layout(const isa_plan_s* p) {
   const size_t tokens = BH * (size_t)p->N * D * elt_size(p->d.dtype);
   w.qr = p->rope ? take(tokens) : 0;
   w.kr = p->rope ? take(tokens) : 0;
+  const size_t n_flat = (size_t)p->info.n_flat, n_ns = (size_t)p->info.n_ns;
+  const bool masked = n_ns > 0 && n_flat > 0;
+  const size_t words = (n_kv + 31) / 32, pairs = (n_flat + 1) / 2, kwg = (n_kv + 1) / 2;
+  w.ns_mask = masked ? take(BH * n_flat * words * sizeof(uint32_t)) : 0;
+  w.tok_list = masked ? take(BH * pairs * 2 * n_ns * sizeof(int32_t)) : 0;
+  w.tok_cnt = masked ? take(BH * pairs * sizeof(int32_t)) : 0;
+  w.fq_off = masked ? take(BH * (kwg + 1) * sizeof(int32_t)) : 0;
+  w.fq_list = masked ? take(BH * n_flat * n_ns * sizeof(int32_t)) : 0;
   w.total = off;
   return w;
 }
@@ -569,13 +579,14 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   if (plan->BH == 0) return ISA_OK;
   const isa_plan_info_t& in = plan->info;
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !aux) return ISA_ERR_INVALID_ARG;
-  if ((in.k > 0 && !aux->sel) || (in.n_flat > 0 && !aux->flat) || (in.n_sharp > 0 && !aux->sharp))
+  const bool masked = in.n_ns > 0 && in.n_flat > 0;
+  if ((in.k > 0 && !aux->sel) || (in.n_flat > 0 && !aux->flat) || (in.n_sharp > 0 && !aux->sharp) ||
+      (masked && !aux->ns))
     return ISA_ERR_INVALID_ARG;
   const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
   for (const void* q : ptrs)
     if (!aligned16(q)) return ISA_ERR_INVALID_ARG;
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
-  if (plan->info.n_ns > 0 && plan->info.n_flat > 0) return ISA_ERR_UNSUPPORTED;
   if (!plan->aligned || plan->d.block != kBlock) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
@@ -621,6 +632,13 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   L.vc = reinterpret_cast<bf16_bits*>(w + W.vc);
   L.dkc = reinterpret_cast<float*>(w + W.dkc);
   L.dvc = reinterpret_cast<float*>(w + W.dvc);
+  L.n_ns = masked ? (int)in.n_ns : 0;
+  L.ns = masked ? aux->ns : nullptr;
+  L.ns_mask = masked ? reinterpret_cast<uint32_t*>(w + W.ns_mask) : nullptr;
+  L.tok_list = masked ? reinterpret_cast<int32_t*>(w + W.tok_list) : nullptr;
+  L.tok_cnt = masked ? reinterpret_cast<int32_t*>(w + W.tok_cnt) : nullptr;
+  L.fq_off = masked ? reinterpret_cast<int32_t*>(w + W.fq_off) : nullptr;
+  L.fq_list = masked ? reinterpret_cast<int32_t*>(w + W.fq_list) : nullptr;
   ISA_LAUNCH(launch_backward(L, s));
   if (plan->rope) {
     // dQ = R^T dQ', dK = R^T dK' (each pair turned back by its angle)

@@ -59,6 +59,22 @@ struct BwdParams {
   const float* dvc_in;
   int64_t dkc_head_stride;  // kv_rows of the Taylor buffers * D
   float inv_w;              // 1 / block weight
+  // block mask inside flat rows (n_ns > 0), tables from bwd_ns_tables_kernel and
+  // bwd_ns_keylists_kernel
+  const uint32_t* ns_mask;  // [BH][n_flat][ns_words]: bit u set if K_new block u is exact
+  int32_t ns_words;         // for flat entry f
+  int32_t n_flat;
+  const int32_t* tok_list;  // [BH][n_pairs][tok_cap]: flat entries 2c, 2c + 1, the union of
+  const int32_t* tok_cnt;   // their exact blocks, ascending, as u * 4 + (bit j: entry 2c + j)
+  int32_t tok_cap;          // 2 n_ns
+  const bf16_bits* k_tok;   // token rows of the exact blocks (K, V) and the original
+  const bf16_bits* v_tok;   // block of each K_new position ([BH][n_kv])
+  const int32_t* kvb_tab;
+  int32_t n_kv;
+  int64_t tok_head_stride;  // N * D
+  const int32_t* fq_off;    // [BH][n_kwg + 1] offsets into fq_list per 128-key group of
+  const int32_t* fq_list;   // K_new: flat query blocks (q * 4 + bit j: key block 2 p + j)
+  int64_t fq_cap;           // n_flat * n_ns entries per head
 };
 
 namespace {
@@ -194,12 +210,18 @@ __device__ __forceinline__ bf16x8_t pack_slots(const f32x4_t& a, const f32x4_t& 
 // dK, dV: a wave owns 16 keys (lane q: key q), a workgroup 128 keys; over the
 // query blocks: S = Q K^T and dP = dO V^T (queries x keys), P, dS = P (dP -
 // delta), dV^T += dO^T P and dK^T += Q^T dS (dims x keys).
-template <int D, bool kRowTable>
+// kMask (block mask inside flat rows): in block-table mode the query blocks
+// are the sharp ones followed by this group's list of flat blocks that take
+// its keys token by token, each with a bit per 64-key half (a half whose bit
+// is clear skips the block: its P is 0); in row-table mode a flat block's
+// exact blocks are masked out of its pooled keys (P = 0).
+template <int D, bool kRowTable, bool kMask = false>
 __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   constexpr int NKK = D / 32;
   constexpr int ND = D / 16;
-  // Q, dO row-major; Q, dO transposed; lse2[64], delta[64]
-  constexpr int kStage = 2 * RS<D>::kBytes + 2 * TS::bytes<D>() + 2 * kBN * 4;
+  // Q, dO row-major; Q, dO transposed; lse2[64], delta[64]; (mask: 4 flag words)
+  constexpr int kFlags = 2 * RS<D>::kBytes + 2 * TS::bytes<D>() + 2 * kBN * 4;
+  constexpr int kStage = kFlags + (kMask ? 16 : 0);
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
 
   const int kv_wgs = (p.kv_rows + 127) / 128;
@@ -235,6 +257,15 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   const float* lseh = p.lse + bh * p.lse_head_stride;
   const float* dlth = p.delta + bh * p.lse_head_stride;
   const int32_t* qtab = p.q_tab + bh * p.q_tab_stride;
+  int n_q = p.n_q_entries;
+  const int32_t* fql = nullptr;
+  if constexpr (kMask && !kRowTable) {
+    const int32_t* off = p.fq_off + bh * (kv_wgs + 1) + kt;
+    fql = p.fq_list + bh * p.fq_cap + off[0];
+    n_q += off[1] - off[0];
+  }
+  const uint32_t* nsm = nullptr;
+  if constexpr (kMask && kRowTable) nsm = p.ns_mask + bh * p.n_flat * p.ns_words;
   // threads 0-255 stage Q, 256-511 stage dO (both layouts).  Two register
   // stages alternate, so a query block's loads are issued two iterations
   // before its LDS copy is written (the LDS holds two blocks: no room for a
@@ -242,14 +273,28 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   const int half = tid >> 8;
   struct Stage {
     Stager16<D> st;
-    float lse;  // thread tid < 64: lse of query row tid; 64..127: delta (as loaded)
+    float lse;       // thread tid < 64: lse of query row tid; 64..127: delta (as loaded)
+    uint32_t fl[4];  // mask (uniform): the block's half bits, or the four words of
+                     // the pooled-key mask that cover this group's 128 keys
   };
   Stage sa, sb;
   sa.st.init(tid & 255);
   sb.st.init(tid & 255);
   sa.lse = sb.lse = 0.0f;
   auto load = [&](Stage& x, int e) __attribute__((always_inline)) {
-    const int64_t r0 = (int64_t)qtab[e] * kBlock;
+    int64_t r0;
+    if constexpr (kMask && !kRowTable) {
+      const int ent = e < p.n_q_entries ? qtab[e] * 4 + 3 : fql[e - p.n_q_entries];
+      r0 = (int64_t)(ent >> 2) * kBlock;
+      x.fl[0] = (uint32_t)(ent & 3);
+    } else {
+      r0 = (int64_t)qtab[e] * kBlock;
+    }
+    if constexpr (kMask && kRowTable) {  // words 4 kt .. 4 kt + 3
+      const uint32_t* row = nsm + (int64_t)e * p.ns_words;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x.fl[j] = row[min(kt * 4 + j, p.ns_words - 1)];
+    }
     auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
     x.st.load(half ? dOh : Qh, row_of);
     // Every thread issues one more load (threads past 127 discard theirs), and
@@ -264,6 +309,10 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
     if (tid < 2 * kBN)
       reinterpret_cast<float*>(b + 2 * RS<D>::kBytes + 2 * TS::bytes<D>())[tid] =
           tid < kBN ? (x.lse - p.lse_offset) * 1.4426950408889634f : x.lse;
+    if constexpr (kMask)
+      if (tid < 4)
+        reinterpret_cast<uint32_t*>(b + kFlags)[tid] =
+            tid == 0 ? x.fl[0] : tid == 1 ? x.fl[1] : tid == 2 ? x.fl[2] : x.fl[3];
   };
 
   f32x4_t dk[ND], dv[ND];
@@ -275,7 +324,6 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
       dv[j][i] = 0.0f;
     }
   const float sl2 = p.scale_log2;
-  const int n_q = p.n_q_entries;
   if (n_q > 0) {
     load(sa, 0);
     store(sa, 0);
@@ -293,53 +341,66 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
     const unsigned char* otr = qtr + TS::bytes<D>();
     const float* lse_s = reinterpret_cast<const float*>(otr + TS::bytes<D>());
     const float* dlt_s = lse_s + kBN;
-
-    // S and dP subtile n: queries 16 n + 4 g + i, key q
-    f32x4_t s[4], dp[4];
+    // mask: a half of the group not in this block's list skips it; a pooled
+    // key that is exact for this flat block has P = 2^-inf = 0 (and dS = 0)
+    bool active = true;
+    float bias = 0.0f;
+    if constexpr (kMask && !kRowTable)
+      active = (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(qt + kFlags)) >>
+                (wave >> 2)) & 1;
+    if constexpr (kMask && kRowTable)
+      bias = ((*reinterpret_cast<const uint32_t*>(qt + kFlags + 4 * (wave >> 1)) >>
+               ((wave & 1) * 16 + q)) & 1) ? -INFINITY : 0.0f;
+    if (active) {
+      // S and dP subtile n: queries 16 n + 4 g + i, key q
+      f32x4_t s[4], dp[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[n][i] = 0.0f;
-        dp[n][i] = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          s[n][i] = 0.0f;
+          dp[n][i] = 0.0f;
+        }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {  // eight independent accumulator chains
+          const int off = RS<D>::off(16 * n + q, (32 * kk + 8 * g) * 2);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qt + off);
+          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[kk], s[n], 0, 0, 0);
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(ot + off);
+          dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, vreg[kk], dp[n], 0, 0, 0);
+        }
       }
+      // P and dS; the query chunk c of the B operands takes subtiles 2c, 2c + 1
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+      for (int n = 0; n < 4; ++n) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 16 * n + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 16 * n + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {  // eight independent accumulator chains
-        const int off = RS<D>::off(16 * n + q, (32 * kk + 8 * g) * 2);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qt + off);
-        s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[kk], s[n], 0, 0, 0);
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(ot + off);
-        dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, vreg[kk], dp[n], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          float x = fmaf(s[n][i], sl2, -lv[i]);
+          if constexpr (kMask && kRowTable) x += bias;
+          const float pr = __builtin_amdgcn_exp2f(x);
+          s[n][i] = pr;
+          dp[n][i] = pr * (dp[n][i] - dv4[i]);
+        }
       }
-    }
-    // P and dS; the query chunk c of the B operands takes subtiles 2c, 2c + 1
+      const bf16x8_t pk0 = pack_slots(s[0], s[1]), pk1 = pack_slots(s[2], s[3]);
+      const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
+      // dV^T += dO^T P, dK^T += Q^T dS: dims 16 j + 4 g + i of key q
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 16 * n + 4 * g);
-      const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + 16 * n + 4 * g);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][i], sl2, -lv[i]));
-        s[n][i] = pr;
-        dp[n][i] = pr * (dp[n][i] - dv4[i]);
+      for (int j = 0; j < ND; ++j) {
+        const bf16x8_t a0 = ts_operand(otr, 16 * j, 0, q, g);
+        dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, pk0, dv[j], 0, 0, 0);
+        const bf16x8_t b0 = ts_operand(qtr, 16 * j, 0, q, g);
+        dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, ds0, dk[j], 0, 0, 0);
+        const bf16x8_t a1 = ts_operand(otr, 16 * j, 1, q, g);
+        dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pk1, dv[j], 0, 0, 0);
+        const bf16x8_t b1 = ts_operand(qtr, 16 * j, 1, q, g);
+        dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, ds1, dk[j], 0, 0, 0);
       }
-    }
-    const bf16x8_t pk0 = pack_slots(s[0], s[1]), pk1 = pack_slots(s[2], s[3]);
-    const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
-    // dV^T += dO^T P, dK^T += Q^T dS: dims 16 j + 4 g + i of key q
-#pragma unroll
-    for (int j = 0; j < ND; ++j) {
-      const bf16x8_t a0 = ts_operand(otr, 16 * j, 0, q, g);
-      dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, pk0, dv[j], 0, 0, 0);
-      const bf16x8_t b0 = ts_operand(qtr, 16 * j, 0, q, g);
-      dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, ds0, dk[j], 0, 0, 0);
-      const bf16x8_t a1 = ts_operand(otr, 16 * j, 1, q, g);
-      dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pk1, dv[j], 0, 0, 0);
-      const bf16x8_t b1 = ts_operand(qtr, 16 * j, 1, q, g);
-      dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, ds1, dk[j], 0, 0, 0);
     }
     if (e + 1 < n_q) store(x, buf ^ 1);
     load(x, min(e + 3, n_q - 1));  // (past the end: a block loaded again, unused)
@@ -402,12 +463,22 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
 // dQ: a wave owns 16 query rows (lane q: query q), a workgroup two 64-row
 // query blocks; over the key tiles: S^T = K Q^T and dP^T = V dO^T (keys x
 // queries), P^T, dS^T, dQ^T += K^T dS^T (dims x queries).
-template <int D, bool kRowTable>
+// kMask (flat rows under the block mask, row-table mode): a flat block's
+// exact blocks are masked out of the pooled key tiles (P = 0), and after
+// them come the token tiles of the union of the two blocks' exact blocks,
+// each with a bit per block (a block whose bit is clear skips the tile).
+// Token terms have weight 1, so their P uses the LSE without the ln w offset.
+template <int D, bool kRowTable, bool kMask = false>
 __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
+  static_assert(!kMask || kRowTable, "the mask applies to the flat rows' pooled keys");
   constexpr int NKK = D / 32;
   constexpr int ND = D / 16;
-  constexpr int kStage = 2 * RS<D>::kBytes + TS::bytes<D>();  // K, V row-major; K transposed
+  // K, V row-major; K transposed; (mask: the tile's block bits)
+  constexpr int kFlags = 2 * RS<D>::kBytes + TS::bytes<D>();
+  constexpr int kStage = kFlags + (kMask ? 16 : 0);
+  constexpr int kMaxWords = kMaxBlocksPerHead / 32;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
+  __shared__ uint32_t nsm_s[kMask ? 2 * kMaxWords : 1];  // the two blocks' mask rows
 
   const int wg_per_head = (p.n_q_entries + 1) / 2;
   bool ok;
@@ -417,7 +488,6 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   const int qt = lid % wg_per_head;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 15, g = lane >> 4;
-
   const int e = qt * 2 + (wave >> 2);
   const bool wave_valid = e < p.n_q_entries;
   const int qblk = wave_valid ? p.q_tab[bh * p.q_tab_stride + e] : 0;
@@ -435,37 +505,73 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   // for the next tile's prefetch loads before every MFMA that reads them.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) asm("" : "+v"(qreg[kk]), "+v"(oreg[kk]));
-  const float lse2 = (p.lse[bh * p.lse_head_stride + qrow] - p.lse_offset) * 1.4426950408889634f;
+  const float lse_raw = p.lse[bh * p.lse_head_stride + qrow];
+  const float lse2 = (lse_raw - p.lse_offset) * 1.4426950408889634f;
+  const float lse2_tok = lse_raw * 1.4426950408889634f;  // token tiles (mask)
   const float dlt = p.delta[bh * p.lse_head_stride + qrow];
 
   const bf16_bits* Kh = p.k + bh * p.kv_head_stride;
   const bf16_bits* Vh = p.v + bh * p.kv_head_stride;
   const int32_t* tab = p.kv_tab + bh * p.kv_tab_stride;
-  const int n_tiles = (p.kv_rows + kBN - 1) / kBN;
+  const int n_rep = (p.kv_rows + kBN - 1) / kBN;  // tiles of the key source
+  int n_tiles = n_rep;
+  const int32_t* tl = nullptr;
+  const int32_t* kvb = nullptr;
+  const bf16_bits *Kt = nullptr, *Vt = nullptr;
+  if constexpr (kMask) {
+    const int64_t pair = bh * wg_per_head + qt;
+    tl = p.tok_list + pair * p.tok_cap;
+    n_tiles += p.tok_cnt[pair];
+    kvb = p.kvb_tab + bh * p.n_kv;
+    Kt = p.k_tok + bh * p.tok_head_stride;
+    Vt = p.v_tok + bh * p.tok_head_stride;
+    for (int i = tid; i < 2 * p.ns_words; i += kT16) {
+      const int j = i / p.ns_words, w = i - j * p.ns_words, f = qt * 2 + j;
+      nsm_s[j * kMaxWords + w] =
+          f < p.n_q_entries ? p.ns_mask[(bh * p.n_flat + f) * p.ns_words + w] : 0u;
+    }
+  }
 
   // threads 0-255 stage K (both layouts), 256-511 stage V (row-major).  Two
   // register stages alternate, so a key tile's loads are issued two
   // iterations before its LDS copy is written.
   const int half = tid >> 8;
-  Stager16<D> sa, sb;
-  sa.init(tid & 255);
-  sb.init(tid & 255);
+  struct Stage {
+    Stager16<D> st;
+    uint32_t fl;  // mask: the token tile's block bits
+  };
+  Stage sa, sb;
+  sa.st.init(tid & 255);
+  sb.st.init(tid & 255);
+  sa.fl = sb.fl = 0u;
   const bf16_bits* src = half ? Vh : Kh;
-  auto load = [&](Stager16<D>& st, int t) __attribute__((always_inline)) {
+  auto load = [&](Stage& x, int t) __attribute__((always_inline)) {
+    if constexpr (kMask) {
+      if (t >= n_rep) {  // token tile of K_new block ent >> 2
+        const int ent = tl[t - n_rep];
+        const int64_t r0 = (int64_t)kvb[ent >> 2] * kBlock;
+        x.fl = (uint32_t)(ent & 3);
+        auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
+        x.st.load(half ? Vt : Kt, row_of);
+        return;
+      }
+    }
     if constexpr (kRowTable) {
       auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
         return tab[min(t * kBN + r, p.kv_rows - 1)];
       };
-      st.load(src, row_of);
+      x.st.load(src, row_of);
     } else {
       const int64_t r0 = (int64_t)tab[t] * kBN;
       auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
-      st.load(src, row_of);
+      x.st.load(src, row_of);
     }
   };
-  auto store = [&](Stager16<D>& st, int buf) __attribute__((always_inline)) {
+  auto store = [&](Stage& x, int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
-    st.store(b + half * RS<D>::kBytes, half ? nullptr : b + 2 * RS<D>::kBytes);
+    x.st.store(b + half * RS<D>::kBytes, half ? nullptr : b + 2 * RS<D>::kBytes);
+    if constexpr (kMask)
+      if (tid == 0) *reinterpret_cast<uint32_t*>(b + kFlags) = x.fl;
   };
 
   f32x4_t dq[ND];
@@ -485,50 +591,68 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   __syncthreads();
   // iteration t computes with key tile t (LDS buffer t & 1), then writes tile
   // t + 1 from stage x into the other buffer and reloads x with tile t + 3
-  auto iteration = [&](int t, Stager16<D>& x) __attribute__((always_inline)) {
+  auto iteration = [&](int t, Stage& x) __attribute__((always_inline)) {
     const int buf = t & 1;
     const unsigned char* kt = smem + buf * kStage;
     const unsigned char* vt = kt + RS<D>::kBytes;
     const unsigned char* ktr = vt + RS<D>::kBytes;
-
-    // S^T and dP^T subtile n: keys 16 n + 4 g + i, query q
-    f32x4_t s[4], dp[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[n][i] = 0.0f;
-        dp[n][i] = 0.0f;
-      }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int off = RS<D>::off(16 * n + q, (32 * kk + 8 * g) * 2);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + off);
-        s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s[n], 0, 0, 0);
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(vt + off);
-        dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, oreg[kk], dp[n], 0, 0, 0);
+    // mask: a token tile not among this block's exact blocks is skipped; a
+    // pooled key that is one of them has P = 0
+    bool active = true, tok = false;
+    uint64_t km = 0;
+    if constexpr (kMask) {
+      tok = t >= n_rep;
+      if (tok) {
+        active = (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(kt + kFlags)) >>
+                  (wave >> 2)) & 1;
+      } else {
+        const uint32_t* m = nsm_s + (wave >> 2) * kMaxWords;
+        km = (uint64_t)m[min(2 * t, p.ns_words - 1)] |
+             ((uint64_t)m[min(2 * t + 1, p.ns_words - 1)] << 32);
       }
     }
-    // keys past the end (only a row-table tile can be partial): P = 0
-    const int valid = p.kv_rows - t * kBN;
+    if (active) {
+      // S^T and dP^T subtile n: keys 16 n + 4 g + i, query q
+      f32x4_t s[4], dp[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][i], sl2, -lse2));
-        const bool live = !kRowTable || 16 * n + 4 * g + i < valid;
-        dp[n][i] = live ? pr * (dp[n][i] - dlt) : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          s[n][i] = 0.0f;
+          dp[n][i] = 0.0f;
+        }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int off = RS<D>::off(16 * n + q, (32 * kk + 8 * g) * 2);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + off);
+          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s[n], 0, 0, 0);
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(vt + off);
+          dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, oreg[kk], dp[n], 0, 0, 0);
+        }
       }
-    const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
-    // dQ^T += K^T dS^T: dims 16 j + 4 g + i of query q
+      // keys past the end (only a row-table tile can be partial): P = 0
+      const int valid = tok ? kBN : p.kv_rows - t * kBN;
+      const float l2 = tok ? lse2_tok : lse2;
 #pragma unroll
-    for (int j = 0; j < ND; ++j) {
-      const bf16x8_t a0 = ts_operand(ktr, 16 * j, 0, q, g);
-      dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ds0, dq[j], 0, 0, 0);
-      const bf16x8_t a1 = ts_operand(ktr, 16 * j, 1, q, g);
-      dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ds1, dq[j], 0, 0, 0);
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * n + 4 * g + i;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][i], sl2, -l2));
+          const bool live = (!kRowTable || key < valid) && !((km >> key) & 1);
+          dp[n][i] = live ? pr * (dp[n][i] - dlt) : 0.0f;
+        }
+      const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
+      // dQ^T += K^T dS^T: dims 16 j + 4 g + i of query q
+#pragma unroll
+      for (int j = 0; j < ND; ++j) {
+        const bf16x8_t a0 = ts_operand(ktr, 16 * j, 0, q, g);
+        dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ds0, dq[j], 0, 0, 0);
+        const bf16x8_t a1 = ts_operand(ktr, 16 * j, 1, q, g);
+        dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ds1, dq[j], 0, 0, 0);
+      }
     }
     if (t + 1 < n_tiles) store(x, buf ^ 1);
     load(x, min(t + 3, n_tiles - 1));
@@ -640,6 +764,91 @@ __global__ __launch_bounds__(kThreads) void bwd_zero_unselected_kernel(
   }
 }
 
+// Block-mask tables of the backward, per (pair c of flat entries, head): the
+// mask rows of entries 2c and 2c + 1 (bit u: K_new block u is exact for the
+// entry) and the ascending union of their exact blocks as u * 4 + bits (bit j:
+// exact for entry 2c + j).  Positions outside [0, n_kv) are ignored.
+__global__ __launch_bounds__(kThreads) void bwd_ns_tables_kernel(
+    const int32_t* __restrict__ ns, int n_flat, int n_ns, int n_kv, int words,
+    uint32_t* __restrict__ mask, int32_t* __restrict__ tok_list, int32_t* __restrict__ tok_cnt) {
+  constexpr int kMaxWords = kMaxBlocksPerHead / 32;
+  __shared__ uint32_t m[2][kMaxWords];
+  __shared__ int pre[kMaxWords + 1];
+  const int c = blockIdx.x, n_pairs = gridDim.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 2 * kMaxWords; i += kThreads) m[i / kMaxWords][i % kMaxWords] = 0u;
+  __syncthreads();
+  for (int i = tid; i < 2 * n_ns; i += kThreads) {
+    const int j = i / n_ns, f = 2 * c + j;
+    if (f < n_flat) {
+      const int u = ns[(bh * n_flat + f) * n_ns + (i - j * n_ns)];
+      if ((unsigned)u < (unsigned)n_kv) atomicOr(&m[j][u >> 5], 1u << (u & 31));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * words; i += kThreads) {
+    const int j = i / words, w = i - j * words, f = 2 * c + j;
+    if (f < n_flat) mask[(bh * n_flat + f) * words + w] = m[j][w];
+  }
+  if (tid < words) pre[tid + 1] = __popc(m[0][tid] | m[1][tid]);
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+  if (tid == 0)
+    for (int w = 1; w <= words; ++w) pre[w] += pre[w - 1];
+  __syncthreads();
+  const int64_t pair = bh * n_pairs + c;
+  if (tid < words) {
+    const uint32_t a = m[0][tid], b = m[1][tid];
+    uint32_t bits = a | b;
+    int32_t* out = tok_list + pair * (2 * (int64_t)n_ns);
+    int pos = pre[tid];
+    while (bits) {
+      const int k = __ffs(bits) - 1;
+      out[pos++] = (tid * 32 + k) * 4 + (int)((a >> k) & 1u) + 2 * (int)((b >> k) & 1u);
+      bits &= bits - 1;
+    }
+  }
+  if (tid == 0) tok_cnt[pair] = pre[words];
+}
+
+// Per head: for every group p of 128 keys of K_new (blocks 2p and 2p + 1), the
+// flat entries whose mask row has either block, ascending, as flat[f] * 4 +
+// bits (bit j: block 2p + j), in CSR form (off[p] .. off[p + 1]).  One thread
+// per group scans the mask rows twice (count, then fill): deterministic.
+constexpr int kListThreads = 1024;
+__global__ __launch_bounds__(kListThreads) void bwd_ns_keylists_kernel(
+    const uint32_t* __restrict__ mask, const int32_t* __restrict__ flat, int n_flat, int words,
+    int n_kwg, int64_t cap, int32_t* __restrict__ off, int32_t* __restrict__ list) {
+  __shared__ int cnt[kMaxBlocksPerHead / 2 + 1];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t* mh = mask + bh * n_flat * words;
+  for (int p = tid; p < n_kwg; p += kListThreads) {
+    const int w = p >> 4, sh = (2 * p) & 31;
+    int c = 0;
+    for (int f = 0; f < n_flat; ++f) c += ((mh[(int64_t)f * words + w] >> sh) & 3u) != 0u;
+    cnt[p + 1] = c;
+  }
+  if (tid == 0) cnt[0] = 0;
+  __syncthreads();
+  if (tid == 0)
+    for (int p = 1; p <= n_kwg; ++p) cnt[p] += cnt[p - 1];
+  __syncthreads();
+  int32_t* oh = off + bh * (n_kwg + 1);
+  int32_t* lh = list + bh * cap;
+  const int32_t* fh = flat + bh * n_flat;
+  for (int p = tid; p <= n_kwg; p += kListThreads) oh[p] = cnt[p];
+  for (int p = tid; p < n_kwg; p += kListThreads) {
+    const int w = p >> 4, sh = (2 * p) & 31;
+    int pos = cnt[p];
+    for (int f = 0; f < n_flat; ++f) {
+      const uint32_t b = (mh[(int64_t)f * words + w] >> sh) & 3u;
+      if (b) lh[pos++] = fh[f] * 4 + (int)b;
+    }
+  }
+}
+
 template <typename Kern>
 hipError_t launch_xcd(Kern kern, int per_head, int BH, const BwdParams& p, hipStream_t s,
                       int threads = kThreads) {
@@ -694,7 +903,37 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
   p.dv = L.dV;
   p.dkc_head_stride = (int64_t)n_kv * D;
 
-  // Taylor path (flat query blocks against the pooled kept blocks)
+  // block mask inside flat rows: tables of the exact blocks per flat block
+  const bool masked = L.n_ns > 0 && L.n_flat > 0;
+  const int words = (n_kv + 31) / 32;
+  const int n_pairs = (L.n_flat + 1) / 2;
+  const int n_kwg = (n_kv + 1) / 2;  // 128-key groups of the exact dK/dV kernel
+  if (masked) {
+    hipLaunchKernelGGL(bwd_ns_tables_kernel, dim3(n_pairs, BH), dim3(kThreads), 0, s, L.ns,
+                       L.n_flat, L.n_ns, n_kv, words, L.ns_mask, L.tok_list, L.tok_cnt);
+    ISA_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(bwd_ns_keylists_kernel, dim3(BH), dim3(kListThreads), 0, s, L.ns_mask,
+                       L.flat, L.n_flat, words, n_kwg, (int64_t)L.n_flat * L.n_ns, L.fq_off,
+                       L.fq_list);
+    ISA_CHECK(hipGetLastError());
+    p.ns_mask = L.ns_mask;
+    p.ns_words = words;
+    p.n_flat = L.n_flat;
+    p.tok_list = L.tok_list;
+    p.tok_cnt = L.tok_cnt;
+    p.tok_cap = 2 * L.n_ns;
+    p.k_tok = L.K;
+    p.v_tok = L.V;
+    p.kvb_tab = L.kv_tab;
+    p.n_kv = n_kv;
+    p.tok_head_stride = (int64_t)L.N * D;
+    p.fq_off = L.fq_off;
+    p.fq_list = L.fq_list;
+    p.fq_cap = (int64_t)L.n_flat * L.n_ns;
+  }
+
+  // Taylor path (flat query blocks against the pooled kept blocks; with the
+  // mask, also the token tiles of their exact blocks in the dQ kernel)
   BwdParams pt = p;
   pt.k = L.kc;
   pt.v = L.vc;
@@ -710,16 +949,22 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
   pt.dkc = L.dkc;
   pt.dvc = L.dvc;
   if (L.n_flat > 0) {
+    const int kg = (n_kv + 127) / 128, qg = (L.n_flat + 1) / 2;
     if (D == 128) {
-      ISA_CHECK(launch_xcd(attn_bwd_dkdv16_kernel<128, true>, (n_kv + 127) / 128, BH, pt, s, kT16));
-      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<128, true>, (L.n_flat + 1) / 2, BH, pt, s, kT16));
+      ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<128, true, true>, kg, BH, pt, s, kT16)
+                       : launch_xcd(attn_bwd_dkdv16_kernel<128, true>, kg, BH, pt, s, kT16));
+      ISA_CHECK(masked ? launch_xcd(attn_bwd_dq16_kernel<128, true, true>, qg, BH, pt, s, kT16)
+                       : launch_xcd(attn_bwd_dq16_kernel<128, true>, qg, BH, pt, s, kT16));
     } else {
-      ISA_CHECK(launch_xcd(attn_bwd_dkdv16_kernel<64, true>, (n_kv + 127) / 128, BH, pt, s, kT16));
-      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<64, true>, (L.n_flat + 1) / 2, BH, pt, s, kT16));
+      ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<64, true, true>, kg, BH, pt, s, kT16)
+                       : launch_xcd(attn_bwd_dkdv16_kernel<64, true>, kg, BH, pt, s, kT16));
+      ISA_CHECK(masked ? launch_xcd(attn_bwd_dq16_kernel<64, true, true>, qg, BH, pt, s, kT16)
+                       : launch_xcd(attn_bwd_dq16_kernel<64, true>, qg, BH, pt, s, kT16));
     }
   }
 
-  // exact path (sharp query blocks against K_new through the block table)
+  // exact path (sharp query blocks against K_new through the block table;
+  // with the mask, then the flat blocks that take these keys token by token)
   BwdParams pe = p;
   pe.k = L.K;
   pe.v = L.V;
@@ -732,14 +977,17 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
   pe.dkc_in = L.n_flat > 0 ? L.dkc : nullptr;
   pe.dvc_in = L.n_flat > 0 ? L.dvc : nullptr;
   pe.inv_w = 1.0f / (float)kBlock;
+  const int eg = (n_kv * kBlock + 127) / 128, sg = (L.n_sharp + 1) / 2;
   if (D == 128) {
-    ISA_CHECK(launch_xcd(attn_bwd_dkdv16_kernel<128, false>, (n_kv * kBlock + 127) / 128, BH, pe, s, kT16));
+    ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<128, false, true>, eg, BH, pe, s, kT16)
+                     : launch_xcd(attn_bwd_dkdv16_kernel<128, false>, eg, BH, pe, s, kT16));
     if (L.n_sharp > 0)
-      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<128, false>, (L.n_sharp + 1) / 2, BH, pe, s, kT16));
+      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<128, false>, sg, BH, pe, s, kT16));
   } else {
-    ISA_CHECK(launch_xcd(attn_bwd_dkdv16_kernel<64, false>, (n_kv * kBlock + 127) / 128, BH, pe, s, kT16));
+    ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<64, false, true>, eg, BH, pe, s, kT16)
+                     : launch_xcd(attn_bwd_dkdv16_kernel<64, false>, eg, BH, pe, s, kT16));
     if (L.n_sharp > 0)
-      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<64, false>, (L.n_sharp + 1) / 2, BH, pe, s, kT16));
+      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<64, false>, sg, BH, pe, s, kT16));
   }
   if (L.n_ctx > 0) {
     if (D == 128)

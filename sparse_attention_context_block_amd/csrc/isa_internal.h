@@ -238,6 +238,12 @@ struct BwdLaunch {
   int32_t *kv_tab, *iota;
   bf16_bits *kc, *vc;
   float *dkc, *dvc;
+  // block mask inside flat rows (n_ns > 0 and n_flat > 0)
+  int n_ns;
+  const int32_t* ns;        // [BH][n_flat][n_ns] exact K_new blocks per flat block
+  uint32_t* ns_mask;        // [BH][n_flat][ceil(n_kv / 32)]
+  int32_t *tok_list, *tok_cnt;  // [BH][ceil(n_flat / 2)][2 n_ns], [BH][ceil(n_flat / 2)]
+  int32_t *fq_off, *fq_list;    // [BH][ceil(n_kv / 2) + 1], [BH][n_flat n_ns]
 };
 
 hipError_t launch_backward(const BwdLaunch& L, hipStream_t stream);

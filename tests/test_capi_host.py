@@ -173,15 +173,40 @@ def test_unaligned_gather_and_backward_unsupported():
     assert st == isa.ISA_ERR_UNSUPPORTED
 
 
-def test_backward_with_block_mask_unsupported():
+def test_backward_with_block_mask_needs_ns():
+    # the block mask's backward reads the forward's ns; a null pointer is
+    # refused before any launch
     lib = isa._lib()
     p = isa.isa_plan_create(1, 2, 256, 256, 128, 64, 0.5, 0.5, 0.25)
+    assert p.info["n_ns"] > 0 and p.info["n_flat"] > 0
     fake = ctypes.c_void_p(0x1000)
     a = isa.isa_aux_t()
     a.sel = a.flat = a.sharp = 0x1000
     st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
                           fake, fake, fake, fake, 1 << 40, None)
-    assert st == isa.ISA_ERR_UNSUPPORTED
+    assert st == isa.ISA_ERR_INVALID_ARG
+
+
+def test_backward_block_mask_workspace():
+    # the mask adds its exact-block tables (mask rows, the dQ pairs' unions,
+    # the key groups' lists) to the backward workspace; too small a workspace
+    # is refused before any launch
+    lib = isa._lib()
+    B, H, L_src, L_ctx = 2, 3, 1024, 3072
+    base = isa.isa_plan_create(B, H, L_src, L_ctx, 128, 64, 0.25, 0.5)
+    p = isa.isa_plan_create(B, H, L_src, L_ctx, 128, 64, 0.25, 0.5, 0.0625)
+    n_flat, n_ns, n_kv = p.info["n_flat"], p.info["n_ns"], p.info["n_kv_blocks"]
+    need = lib.isa_backward_workspace_bytes(p.handle)
+    extra = need - lib.isa_backward_workspace_bytes(base.handle)
+    tables = 4 * B * H * (n_flat * ((n_kv + 31) // 32) + ((n_flat + 1) // 2) * (2 * n_ns + 1)
+                          + (n_kv + 1) // 2 + 1 + n_flat * n_ns)
+    assert tables <= extra <= tables + 5 * 256
+    fake = ctypes.c_void_p(0x1000)
+    a = isa.isa_aux_t()
+    a.sel = a.flat = a.sharp = a.ns = 0x1000
+    st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
+                          fake, fake, fake, fake, need - 1, None)
+    assert st == isa.ISA_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("base", [-1.0, float("nan"), float("inf")])

@@ -28,8 +28,8 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f):
-    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, 64, alpha_s, alpha_f)
+def _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f, alpha_ns=0.0):
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, 64, alpha_s, alpha_f, alpha_ns)
     q, k, v, do = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v", "do"))
     o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
     dq, dk, dv = isa.isa_backward(plan, q, k, v, o, do, lse, aux)
@@ -72,6 +72,41 @@ def test_backward_small_full_parity(B, H, L_src, L_ctx, D, alpha_s, alpha_f, see
                     assert not dk[bi, h, L_src + 64 * j:L_src + 64 * (j + 1)].any()
 
 
+@pytest.mark.parametrize("B,H,L_src,L_ctx,D,alpha_s,alpha_f,alpha_ns,seed", [
+    (1, 2, 1024, 1024, 128, 0.5, 0.5, 0.0625, 61),  # the pages' ratio: 2 of 24 blocks exact
+    (1, 3, 640, 448, 128, 0.25, 0.45, 0.25, 62),    # 7 flat blocks: a lone dQ pair member
+    (2, 2, 1024, 768, 64, 0.34, 0.3, 0.2, 63),      # D = 64, B = 2, N_K' = 21: a half key group
+    (1, 2, 1024, 1024, 128, 0.5, 1.0, 0.125, 64),   # every block flat: no sharp rows
+    (1, 2, 512, 512, 128, 0.5, 0.5, 1.0, 65),       # every kept block exact in flat rows
+])
+def test_backward_block_mask_parity(B, H, L_src, L_ctx, D, alpha_s, alpha_f, alpha_ns, seed):
+    """The block mask inside flat rows: the GPU backward against isa_ref_bwd
+    with the forward's ns."""
+    _say(f"bwd mask B{B} H{H} L_src{L_src} L_ctx{L_ctx} D{D} as{alpha_s} af{alpha_f} "
+         f"ans{alpha_ns} seed{seed}")
+    inp = generate(B, H, L_src, L_ctx, D, 64, seed=seed, variant="icl", grad=True)
+    plan, grads, aux = _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f, alpha_ns)
+    assert plan.info["n_ns"] > 0 and plan.info["n_flat"] > 0
+    ref = orc.isa_ref_bwd(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v", "do")),
+                          L_src, L_ctx, 64, aux["sel"], aux["flat"], aux["ns"])
+    _check_grads([out_f64(g) for g in grads], ref, "mask")
+    dk = out_f64(grads[1])
+    for bi in range(B):
+        for h in range(H):
+            for j in range(L_ctx // 64):
+                if j not in aux["sel"][bi, h]:
+                    assert not dk[bi, h, L_src + 64 * j:L_src + 64 * (j + 1)].any()
+
+
+def test_backward_block_mask_deterministic():
+    _say("bwd mask determinism B1 H2 N2048 ans 0.0625 seed 66")
+    inp = generate(1, 2, 1024, 1024, 128, 64, seed=66, variant="icl", grad=True)
+    _, g1, _ = _fwd_bwd(inp, 1, 2, 1024, 1024, 128, 0.25, 0.5, 0.0625)
+    _, g2, _ = _fwd_bwd(inp, 1, 2, 1024, 1024, 128, 0.25, 0.5, 0.0625)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_backward_all_kept_all_exact_is_dense_backward():
     _say("bwd as1 af0 vs dense backward, seed 48")
     inp = generate(1, 2, 512, 512, 128, 64, seed=48, variant="icl", grad=True)
@@ -108,6 +143,34 @@ def test_backward_workload_b2_n16384():
     # sums to one, each dS row to zero, and the Taylor broadcast gives every
     # token of block j the share dV^c_j / w_j), to the rounding of the bf16
     # operands and outputs, compared with the root sum of squares of the terms
+    dk, dv = got[1], got[2]
+    do = to_f64(inp["do"], "bf16")
+    err_v = np.abs(dv.sum(axis=2) - do.sum(axis=2)) / np.sqrt((dv ** 2).sum(axis=2)
+                                                              + (do ** 2).sum(axis=2))
+    err_k = np.abs(dk.sum(axis=2)) / np.sqrt((dk ** 2).sum(axis=2))
+    assert err_v.max() <= 0.05 and err_k.max() <= 0.05, (err_v.max(), err_k.max())
+    _say(f"every head: |sum dV - sum dO| / RSS max {err_v.max():.2e}, "
+         f"|sum dK| / RSS max {err_k.max():.2e}")
+
+
+def test_backward_block_mask_workload_b2_n16384():
+    """The backward workload with the block mask at the pages' ratio
+    alpha_ns = 0.0625: two heads (one per batch entry) in full against the
+    oracle, every head by the gradient-sum identities."""
+    c = CONFIGS["isa_fwd_bwd_bf16_B2_N16384"]
+    B, H, L_src, L_ctx, D = c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"]
+    _say(f"bwd mask workload {c['name']} ans 0.0625 seed {c['seed']}")
+    inp = generate_config("isa_fwd_bwd_bf16_B2_N16384")
+    plan, grads, aux = _fwd_bwd(inp, B, H, L_src, L_ctx, D, c["alpha_s"], c["alpha_f"], 0.0625)
+    assert plan.info["n_ns"] > 0
+    got = [out_f64(g) for g in grads]
+    for g in got:
+        assert np.isfinite(g).all()
+    for bi, h in ((0, 17), (1, 6)):
+        sl = (slice(bi, bi + 1), slice(h, h + 1))
+        ref = orc.isa_ref_bwd(*(to_f64(inp[x][sl], "bf16") for x in ("q", "k", "v", "do")),
+                              L_src, L_ctx, 64, aux["sel"][sl], aux["flat"][sl], aux["ns"][sl])
+        _check_grads([g[sl] for g in got], ref, f"mask head ({bi},{h})")
     dk, dv = got[1], got[2]
     do = to_f64(inp["do"], "bf16")
     err_v = np.abs(dv.sum(axis=2) - do.sum(axis=2)) / np.sqrt((dv ** 2).sum(axis=2)
