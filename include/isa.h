@@ -240,8 +240,10 @@ isa_status_t isa_dense_forward(int32_t B, int32_t H, int32_t N, int32_t D, isa_d
  * holds the rotated Q and K, two [B, H, N, D] copies; with the block mask,
  * the exact-block tables: about B * H * n_flat * (n_ns + n_kv / 32) * 4 bytes).
  * Errors: ISA_ERR_INVALID_ARG (also a null aux->ns with the block mask),
- * ISA_ERR_UNSUPPORTED (FP32, block != 64, or L_src / L_ctx not a multiple of
- * 64), ISA_ERR_WORKSPACE, ISA_ERR_HIP. */
+ * ISA_ERR_UNSUPPORTED (FP32), ISA_ERR_WORKSPACE, ISA_ERR_HIP.  Any plan
+ * isa_plan_create accepts is taken otherwise: partial blocks (L_src or L_ctx
+ * not a multiple of b; a block of w tokens enters the Taylor path with weight
+ * w and its mean over those w rows) and b = 32, 64, 128. */
 isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const void* V,
                           const void* O, const void* dO, const float* lse, const isa_aux_t* aux,
                           void* dQ, void* dK, void* dV,

@@ -587,7 +587,6 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   for (const void* q : ptrs)
     if (!aligned16(q)) return ISA_ERR_INVALID_ARG;
   if (plan->d.dtype != ISA_DTYPE_BF16) return ISA_ERR_UNSUPPORTED;
-  if (!plan->aligned || plan->d.block != kBlock) return ISA_ERR_UNSUPPORTED;
   const BwdLayout W = bwd_layout(plan);
   if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return ISA_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);
@@ -596,6 +595,7 @@ isa_status_t isa_backward(isa_plan_t plan, const void* Q, const void* K, const v
   L.D = plan->d.D;
   L.N = (int)plan->N;
   L.L_src = plan->d.L_src;
+  L.block = plan->d.block;
   L.n_src = (int)in.n_src_blocks;
   L.n_ctx = (int)in.n_ctx_blocks;
   L.k = (int)in.k;

@@ -75,12 +75,40 @@ struct BwdParams {
   const int32_t* fq_off;    // [BH][n_kwg + 1] offsets into fq_list per 128-key group of
   const int32_t* fq_list;   // K_new: flat query blocks (q * 4 + bit j: key block 2 p + j)
   int64_t fq_cap;           // n_flat * n_ns entries per head
+  // general blocks (partial blocks, b != 64): a 64-row tile is two 32-row
+  // slices of a block list (list_slice); the entries and key rows count tiles
+  BlockGrid grid;
+  int32_t shift;            // log2(b / 32)
+  int32_t q_slices;         // slices of the query list (its blocks << shift)
+  int32_t kv_slices;        // slices of K_new (n_kv << shift)
 };
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBN = 64;
+
+// A 64-row tile as two 32-row slices (start, valid rows); rows past a
+// slice's count read its last valid row (or its start when it is empty, which
+// list_slice keeps inside the head) and count as invalid.
+struct TileRows {
+  int32_t s0, c0, s1, c1;
+  __device__ __forceinline__ int64_t row(int r) const {
+    const int i = r & 31, c = r < 32 ? c0 : c1;
+    return (int64_t)(r < 32 ? s0 : s1) + (i < c ? i : (c > 0 ? c - 1 : 0));
+  }
+  __device__ __forceinline__ bool valid(int r) const { return (r & 31) < (r < 32 ? c0 : c1); }
+};
+__device__ __forceinline__ TileRows tile_rows(const BlockGrid& g, const int32_t* list,
+                                              int n_slices, int shift, int tile) {
+  const Slice a = list_slice(g, list, n_slices, shift, 2 * tile);
+  const Slice b = list_slice(g, list, n_slices, shift, 2 * tile + 1);
+  return TileRows{a.start, a.cnt, b.start, b.cnt};
+}
+// the one tile of block blk at b = 64
+__device__ __forceinline__ TileRows block_tile64(const BlockGrid& g, int blk) {
+  return tile_rows(g, nullptr, 0x7fffffff, 1, blk);
+}
 // native vector (not HIP's uint4 struct) so staging registers never leave VGPRs
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -215,7 +243,11 @@ __device__ __forceinline__ bf16x8_t pack_slots(const f32x4_t& a, const f32x4_t& 
 // its keys token by token, each with a bit per 64-key half (a half whose bit
 // is clear skips the block: its P is 0); in row-table mode a flat block's
 // exact blocks are masked out of its pooled keys (P = 0).
-template <int D, bool kRowTable, bool kMask = false>
+// kGen (partial blocks, b != 64): query entries and block-table keys are
+// 64-row tiles of two 32-row slices; rows past a slice's count are invalid
+// (a query row gets P = 0 through an infinite LSE, a key is not written), and
+// a pooled key's weight w_j enters as log2(w_j / b) in its exponent.
+template <int D, bool kRowTable, bool kMask = false, bool kGen = false>
 __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   constexpr int NKK = D / 32;
   constexpr int ND = D / 16;
@@ -236,10 +268,22 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   // this wave's 16 keys (virtual rows of K_new); lane (q, g) holds dims
   // 32 kk + 8 g .. + 7 of key q
   const int vrow = kt * 128 + wave * 16 + q;
-  const bool key_valid = vrow < p.kv_rows;
+  bool key_valid = vrow < p.kv_rows;
   const int32_t* tab = p.kv_tab + bh * p.kv_tab_stride;
   const int vr = min(vrow, p.kv_rows - 1);
-  const int64_t krow = kRowTable ? (int64_t)tab[vr] : (int64_t)tab[vr >> 6] * kBN + (vr & 63);
+  int64_t krow;
+  float wbias = 0.0f;  // kGen, row-table: log2(w_j / b) of this pooled key
+  if constexpr (kRowTable) {
+    krow = tab[vr];
+    if constexpr (kGen)
+      wbias = log2f((float)p.grid.rows(p.kvb_tab[bh * p.n_kv + vr]) / (float)p.grid.len);
+  } else if constexpr (kGen) {
+    const TileRows tr = tile_rows(p.grid, tab, p.kv_slices, p.shift, vr >> 6);
+    krow = tr.row(vr & 63);
+    key_valid = key_valid && tr.valid(vr & 63);
+  } else {
+    krow = (int64_t)tab[vr >> 6] * kBN + (vr & 63);
+  }
   const bf16_bits* Kh = p.k + bh * p.kv_head_stride;
   const bf16_bits* Vh = p.v + bh * p.kv_head_stride;
   bf16x8_t kreg[NKK], vreg[NKK];
@@ -276,12 +320,39 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
     float lse;       // thread tid < 64: lse of query row tid; 64..127: delta (as loaded)
     uint32_t fl[4];  // mask (uniform): the block's half bits, or the four words of
                      // the pooled-key mask that cover this group's 128 keys
+    bool qv;         // kGen: query row tid & 63 is inside its slice
   };
   Stage sa, sb;
   sa.st.init(tid & 255);
   sb.st.init(tid & 255);
   sa.lse = sb.lse = 0.0f;
+  sa.qv = sb.qv = true;
   auto load = [&](Stage& x, int e) __attribute__((always_inline)) {
+    if constexpr (kMask && kRowTable) {  // words 4 kt .. 4 kt + 3
+      const uint32_t* row = nsm + (int64_t)e * p.ns_words;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x.fl[j] = row[min(kt * 4 + j, p.ns_words - 1)];
+    }
+    if constexpr (kGen) {
+      TileRows tr;
+      if constexpr (kMask && !kRowTable) {
+        if (e < p.n_q_entries) {
+          tr = tile_rows(p.grid, qtab, p.q_slices, p.shift, e);
+          x.fl[0] = 3u;
+        } else {
+          const int ent = fql[e - p.n_q_entries];
+          tr = block_tile64(p.grid, ent >> 2);
+          x.fl[0] = (uint32_t)(ent & 3);
+        }
+      } else {
+        tr = tile_rows(p.grid, qtab, p.q_slices, p.shift, e);
+      }
+      auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return tr.row(r); };
+      x.st.load(half ? dOh : Qh, row_of);
+      x.lse = (tid & kBN ? dlth : lseh)[tr.row(tid & (kBN - 1))];
+      x.qv = tr.valid(tid & (kBN - 1));
+      return;
+    }
     int64_t r0;
     if constexpr (kMask && !kRowTable) {
       const int ent = e < p.n_q_entries ? qtab[e] * 4 + 3 : fql[e - p.n_q_entries];
@@ -289,11 +360,6 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
       x.fl[0] = (uint32_t)(ent & 3);
     } else {
       r0 = (int64_t)qtab[e] * kBlock;
-    }
-    if constexpr (kMask && kRowTable) {  // words 4 kt .. 4 kt + 3
-      const uint32_t* row = nsm + (int64_t)e * p.ns_words;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x.fl[j] = row[min(kt * 4 + j, p.ns_words - 1)];
     }
     auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
     x.st.load(half ? dOh : Qh, row_of);
@@ -306,9 +372,12 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
   auto store = [&](Stage& x, int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
     x.st.store(b + half * RS<D>::kBytes, b + 2 * RS<D>::kBytes + half * TS::bytes<D>());
-    if (tid < 2 * kBN)
-      reinterpret_cast<float*>(b + 2 * RS<D>::kBytes + 2 * TS::bytes<D>())[tid] =
-          tid < kBN ? (x.lse - p.lse_offset) * 1.4426950408889634f : x.lse;
+    if (tid < 2 * kBN) {
+      float l = tid < kBN ? (x.lse - p.lse_offset) * 1.4426950408889634f : x.lse;
+      if constexpr (kGen)  // a row outside its slice: P = 2^-inf = 0
+        if (tid < kBN && !x.qv) l = INFINITY;
+      reinterpret_cast<float*>(b + 2 * RS<D>::kBytes + 2 * TS::bytes<D>())[tid] = l;
+    }
     if constexpr (kMask)
       if (tid < 4)
         reinterpret_cast<uint32_t*>(b + kFlags)[tid] =
@@ -344,13 +413,13 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
     // mask: a half of the group not in this block's list skips it; a pooled
     // key that is exact for this flat block has P = 2^-inf = 0 (and dS = 0)
     bool active = true;
-    float bias = 0.0f;
+    float bias = wbias;
     if constexpr (kMask && !kRowTable)
       active = (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(qt + kFlags)) >>
                 (wave >> 2)) & 1;
     if constexpr (kMask && kRowTable)
       bias = ((*reinterpret_cast<const uint32_t*>(qt + kFlags + 4 * (wave >> 1)) >>
-               ((wave & 1) * 16 + q)) & 1) ? -INFINITY : 0.0f;
+               ((wave & 1) * 16 + q)) & 1) ? -INFINITY : wbias;
     if (active) {
       // S and dP subtile n: queries 16 n + 4 g + i, key q
       f32x4_t s[4], dp[4];
@@ -381,7 +450,7 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = fmaf(s[n][i], sl2, -lv[i]);
-          if constexpr (kMask && kRowTable) x += bias;
+          if constexpr ((kMask || kGen) && kRowTable) x += bias;
           const float pr = __builtin_amdgcn_exp2f(x);
           s[n][i] = pr;
           dp[n][i] = pr * (dp[n][i] - dv4[i]);
@@ -428,12 +497,16 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
     }
   } else {
     // the Taylor path's pooled gradient of this key's block, spread over its tokens
-    const int blk = vrow >> 6;
+    int blk = vrow >> 6;  // K_new position of the key's block
+    float iw = p.inv_w;
+    if constexpr (kGen) {
+      blk = (2 * (vrow >> 6) + ((vrow & 63) >> 5)) >> p.shift;
+      iw = 1.0f / (float)p.grid.rows(tab[blk]);
+    }
     const float* tk = p.dkc_in ? p.dkc_in + bh * p.dkc_head_stride + (int64_t)blk * D : nullptr;
     const float* tv = p.dvc_in ? p.dvc_in + bh * p.dkc_head_stride + (int64_t)blk * D : nullptr;
     bf16_bits* dKh = p.dk + bh * p.q_head_stride + krow * D;
     bf16_bits* dVh = p.dv + bh * p.q_head_stride + krow * D;
-    const float iw = p.inv_w;
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
       const int d0 = 16 * j + 4 * g;
@@ -468,17 +541,24 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
 // them come the token tiles of the union of the two blocks' exact blocks,
 // each with a bit per block (a block whose bit is clear skips the tile).
 // Token terms have weight 1, so their P uses the LSE without the ln w offset.
-template <int D, bool kRowTable, bool kMask = false>
+// kGen (partial blocks, b != 64): query entries and block-table key tiles are
+// 64-row tiles of two 32-row slices; a query row outside its slice is not
+// written, a key outside its slice has P = 0, and a pooled key's weight w_j
+// enters as log2(w_j / b) in its exponent.
+template <int D, bool kRowTable, bool kMask = false, bool kGen = false>
 __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   static_assert(!kMask || kRowTable, "the mask applies to the flat rows' pooled keys");
   constexpr int NKK = D / 32;
   constexpr int ND = D / 16;
-  // K, V row-major; K transposed; (mask: the tile's block bits)
+  // K, V row-major; K transposed; (mask or general blocks: the tile's flag word)
+  constexpr bool kFlagWord = kMask || (kGen && !kRowTable);
   constexpr int kFlags = 2 * RS<D>::kBytes + TS::bytes<D>();
-  constexpr int kStage = kFlags + (kMask ? 16 : 0);
+  constexpr int kStage = kFlags + (kFlagWord ? 16 : 0);
   constexpr int kMaxWords = kMaxBlocksPerHead / 32;
+  constexpr bool kWeights = kGen && kRowTable;  // per pooled key log2(w_j / b)
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
   __shared__ uint32_t nsm_s[kMask ? 2 * kMaxWords : 1];  // the two blocks' mask rows
+  __shared__ __attribute__((aligned(16))) float lw_s[kWeights ? kMaxBlocksPerHead + kBN : 1];
 
   const int wg_per_head = (p.n_q_entries + 1) / 2;
   bool ok;
@@ -489,9 +569,16 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 15, g = lane >> 4;
   const int e = qt * 2 + (wave >> 2);
-  const bool wave_valid = e < p.n_q_entries;
-  const int qblk = wave_valid ? p.q_tab[bh * p.q_tab_stride + e] : 0;
-  const int64_t qrow = (int64_t)qblk * kBlock + (wave & 3) * 16 + q;
+  bool wave_valid = e < p.n_q_entries;
+  int64_t qrow;
+  if constexpr (kGen) {  // entry e: tile e of the query list
+    const TileRows tr = tile_rows(p.grid, p.q_tab + bh * p.q_tab_stride, p.q_slices, p.shift, e);
+    qrow = tr.row((wave & 3) * 16 + q);
+    wave_valid = wave_valid && tr.valid((wave & 3) * 16 + q);  // (per lane)
+  } else {
+    const int qblk = wave_valid ? p.q_tab[bh * p.q_tab_stride + e] : 0;
+    qrow = (int64_t)qblk * kBlock + (wave & 3) * 16 + q;
+  }
   const bf16_bits* Qh = p.q + bh * p.q_head_stride;
   const bf16_bits* dOh = p.dout + bh * p.q_head_stride;
   bf16x8_t qreg[NKK], oreg[NKK];
@@ -531,6 +618,12 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
           f < p.n_q_entries ? p.ns_mask[(bh * p.n_flat + f) * p.ns_words + w] : 0u;
     }
   }
+  if constexpr (kWeights) {
+    const int32_t* kvb_h = p.kvb_tab + bh * p.n_kv;
+    const float inv_len = 1.0f / (float)p.grid.len;
+    for (int u = tid; u < n_rep * kBN; u += kT16)
+      lw_s[u] = u < p.n_kv ? log2f((float)p.grid.rows(kvb_h[u]) * inv_len) : 0.0f;
+  }
 
   // threads 0-255 stage K (both layouts), 256-511 stage V (row-major).  Two
   // register stages alternate, so a key tile's loads are issued two
@@ -538,7 +631,8 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   const int half = tid >> 8;
   struct Stage {
     Stager16<D> st;
-    uint32_t fl;  // mask: the token tile's block bits
+    uint32_t fl;  // bits 0-1: a token tile's block bits (mask); 8-15, 16-23: the
+                  // valid rows of the tile's two slices (general blocks)
   };
   Stage sa, sb;
   sa.st.init(tid & 255);
@@ -549,12 +643,26 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
     if constexpr (kMask) {
       if (t >= n_rep) {  // token tile of K_new block ent >> 2
         const int ent = tl[t - n_rep];
-        const int64_t r0 = (int64_t)kvb[ent >> 2] * kBlock;
-        x.fl = (uint32_t)(ent & 3);
-        auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
-        x.st.load(half ? Vt : Kt, row_of);
+        if constexpr (kGen) {
+          const TileRows tr = block_tile64(p.grid, kvb[ent >> 2]);
+          x.fl = (uint32_t)(ent & 3) | ((uint32_t)tr.c0 << 8) | ((uint32_t)tr.c1 << 16);
+          auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return tr.row(r); };
+          x.st.load(half ? Vt : Kt, row_of);
+        } else {
+          const int64_t r0 = (int64_t)kvb[ent >> 2] * kBlock;
+          x.fl = (uint32_t)(ent & 3);
+          auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return r0 + r; };
+          x.st.load(half ? Vt : Kt, row_of);
+        }
         return;
       }
+    }
+    if constexpr (kGen && !kRowTable) {  // tile t of K_new
+      const TileRows tr = tile_rows(p.grid, tab, p.kv_slices, p.shift, t);
+      x.fl = ((uint32_t)tr.c0 << 8) | ((uint32_t)tr.c1 << 16);
+      auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t { return tr.row(r); };
+      x.st.load(src, row_of);
+      return;
     }
     if constexpr (kRowTable) {
       auto row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
@@ -570,7 +678,7 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   auto store = [&](Stage& x, int buf) __attribute__((always_inline)) {
     unsigned char* b = smem + buf * kStage;
     x.st.store(b + half * RS<D>::kBytes, half ? nullptr : b + 2 * RS<D>::kBytes);
-    if constexpr (kMask)
+    if constexpr (kFlagWord)
       if (tid == 0) *reinterpret_cast<uint32_t*>(b + kFlags) = x.fl;
   };
 
@@ -600,11 +708,13 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
     // pooled key that is one of them has P = 0
     bool active = true, tok = false;
     uint64_t km = 0;
+    uint32_t fw = 0;  // the tile's flag word
+    if constexpr (kFlagWord)
+      fw = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(kt + kFlags));
     if constexpr (kMask) {
       tok = t >= n_rep;
       if (tok) {
-        active = (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(kt + kFlags)) >>
-                  (wave >> 2)) & 1;
+        active = (fw >> (wave >> 2)) & 1;
       } else {
         const uint32_t* m = nsm_s + (wave >> 2) * kMaxWords;
         km = (uint64_t)m[min(2 * t, p.ns_words - 1)] |
@@ -632,18 +742,33 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
           dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, oreg[kk], dp[n], 0, 0, 0);
         }
       }
-      // keys past the end (only a row-table tile can be partial): P = 0
+      // keys past the end (only a row-table tile can be partial, or, with
+      // general blocks, any tile past its slices' counts): P = 0
       const int valid = tok ? kBN : p.kv_rows - t * kBN;
       const float l2 = tok ? lse2_tok : lse2;
+      const bool by_slices = kGen && (!kRowTable || tok);
+      const int c0 = (fw >> 8) & 0xff, c1 = (fw >> 16) & 0xff;
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 4; ++n) {
+        float4 wb = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (kWeights)
+          if (!tok) wb = *reinterpret_cast<const float4*>(lw_s + t * kBN + 16 * n + 4 * g);
+        const float wbi[4] = {wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * n + 4 * g + i;
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][i], sl2, -l2));
-          const bool live = (!kRowTable || key < valid) && !((km >> key) & 1);
+          float x = fmaf(s[n][i], sl2, -l2);
+          if constexpr (kWeights) x += wbi[i];
+          const float pr = __builtin_amdgcn_exp2f(x);
+          bool live;
+          if constexpr (kGen)
+            live = by_slices ? (key < 32 ? key < c0 : key - 32 < c1) : key < valid;
+          else
+            live = !kRowTable || key < valid;
+          live = live && !((km >> key) & 1);
           dp[n][i] = live ? pr * (dp[n][i] - dlt) : 0.0f;
         }
+      }
       const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
       // dQ^T += K^T dS^T: dims 16 j + 4 g + i of query q
 #pragma unroll
@@ -704,15 +829,16 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16_bits* __
 }
 
 // Per (kept block t, head): block table entry and the bf16 means of the block's
-// K and V rows (fp64 sums, rounded as the forward's pooling rounds them).
+// K and V rows (fp64 sums divided by the block's length, rounded as the
+// forward's pooling rounds them).
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const bf16_bits* __restrict__ K, const bf16_bits* __restrict__ V,
-    const int32_t* __restrict__ sel, int N, int n_src, int k, int32_t* __restrict__ kv_tab,
+    const int32_t* __restrict__ sel, BlockGrid grid, int k, int32_t* __restrict__ kv_tab,
     int32_t* __restrict__ iota, bf16_bits* __restrict__ kc, bf16_bits* __restrict__ vc) {
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  const int n_kv = n_src + k;
+  const int n_src = grid.n_src, n_kv = n_src + k;
   const int blk = t < n_src ? t : n_src + sel[bh * k + (t - n_src)];
   if (threadIdx.x == 0) {
     kv_tab[bh * n_kv + t] = blk;
@@ -723,10 +849,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   const int d = tid % D;
   const int g = tid / D;           // row group
   constexpr int G = kThreads / D;  // row groups
-  const bf16_bits* kb = K + (bh * N + (int64_t)blk * kBlock) * D;
-  const bf16_bits* vb = V + (bh * N + (int64_t)blk * kBlock) * D;
+  const int rows = grid.rows(blk);
+  const bf16_bits* kb = K + (bh * grid.N + grid.start(blk)) * D;
+  const bf16_bits* vb = V + (bh * grid.N + grid.start(blk)) * D;
   double sk = 0.0, sv = 0.0;
-  for (int r = g; r < kBlock; r += G) {
+  for (int r = g; r < rows; r += G) {
     sk += (double)__uint_as_float((uint32_t)kb[r * D + d] << 16);
     sv += (double)__uint_as_float((uint32_t)vb[r * D + d] << 16);
   }
@@ -741,24 +868,25 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       b += red[1][i][tid];
     }
     const int64_t o = (bh * n_kv + t) * (int64_t)D + tid;
-    kc[o] = (bf16_bits)bf16_bits_rne(a * (1.0 / kBlock));  // as the forward's pooling rounds
-    vc[o] = (bf16_bits)bf16_bits_rne(b * (1.0 / kBlock));
+    kc[o] = (bf16_bits)bf16_bits_rne(a / (double)rows);  // as the forward's pooling rounds
+    vc[o] = (bf16_bits)bf16_bits_rne(b / (double)rows);
   }
 }
 
 // dK, dV rows of context blocks that were not kept are zero.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_zero_unselected_kernel(
-    const int32_t* __restrict__ sel, int N, int L_src, int k, bf16_bits* __restrict__ dK,
+    const int32_t* __restrict__ sel, BlockGrid grid, int k, bf16_bits* __restrict__ dK,
     bf16_bits* __restrict__ dV) {
   const int j = blockIdx.x;  // context block
   const int64_t bh = blockIdx.y;
   for (int i = 0; i < k; ++i)
     if (sel[bh * k + i] == j) return;  // kept: written by the exact kernel
-  uint4* a = reinterpret_cast<uint4*>(dK + (bh * N + L_src + (int64_t)j * kBlock) * D);
-  uint4* b = reinterpret_cast<uint4*>(dV + (bh * N + L_src + (int64_t)j * kBlock) * D);
+  const int blk = grid.n_src + j;
+  uint4* a = reinterpret_cast<uint4*>(dK + (bh * grid.N + grid.start(blk)) * D);
+  uint4* b = reinterpret_cast<uint4*>(dV + (bh * grid.N + grid.start(blk)) * D);
   const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int i = threadIdx.x; i < kBlock * D / 8; i += kThreads) {
+  for (int i = threadIdx.x; i < grid.rows(blk) * D / 8; i += kThreads) {
     a[i] = z;
     b[i] = z;
   }
@@ -860,6 +988,30 @@ hipError_t launch_xcd(Kern kern, int per_head, int BH, const BwdParams& p, hipSt
 
 }  // namespace
 
+// The attention kernels of one head dimension: Taylor dK^c/dV^c and flat-row
+// dQ, then exact dK/dV and sharp-row dQ, each in the variant the plan needs.
+template <int D, bool kGen>
+hipError_t launch_paths(const BwdParams& pt, const BwdParams& pe, bool masked, int n_flat_tiles,
+                        int n_sharp_tiles, int n_kv, int key_tiles, int BH, hipStream_t s) {
+  hipError_t e;
+  if (n_flat_tiles > 0) {
+    const int kg = (n_kv + 127) / 128, qg = (n_flat_tiles + 1) / 2;
+    e = masked ? launch_xcd(attn_bwd_dkdv16_kernel<D, true, true, kGen>, kg, BH, pt, s, kT16)
+               : launch_xcd(attn_bwd_dkdv16_kernel<D, true, false, kGen>, kg, BH, pt, s, kT16);
+    if (e != hipSuccess) return e;
+    e = masked ? launch_xcd(attn_bwd_dq16_kernel<D, true, true, kGen>, qg, BH, pt, s, kT16)
+               : launch_xcd(attn_bwd_dq16_kernel<D, true, false, kGen>, qg, BH, pt, s, kT16);
+    if (e != hipSuccess) return e;
+  }
+  const int eg = (key_tiles * kBN + 127) / 128, sg = (n_sharp_tiles + 1) / 2;
+  e = masked ? launch_xcd(attn_bwd_dkdv16_kernel<D, false, true, kGen>, eg, BH, pe, s, kT16)
+             : launch_xcd(attn_bwd_dkdv16_kernel<D, false, false, kGen>, eg, BH, pe, s, kT16);
+  if (e != hipSuccess) return e;
+  if (n_sharp_tiles > 0)
+    return launch_xcd(attn_bwd_dq16_kernel<D, false, false, kGen>, sg, BH, pe, s, kT16);
+  return hipSuccess;
+}
+
 // Backward launch sequence (see the top of this file).
 hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
   const int BH = L.BH, D = L.D;
@@ -876,14 +1028,28 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
                          dim3(kThreads), 0, s, L.O, L.dO, rows, L.delta);
     ISA_CHECK(hipGetLastError());
   }
+  BlockGrid grid;
+  grid.L_src = L.L_src;
+  grid.n_src = L.n_src;
+  grid.N = L.N;
+  grid.len = L.block;
   const int n_kv = L.n_src + L.k;
   if (D == 128)
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(n_kv, BH), dim3(kThreads), 0, s, L.K, L.V,
-                       L.sel, L.N, L.n_src, L.k, L.kv_tab, L.iota, L.kc, L.vc);
+                       L.sel, grid, L.k, L.kv_tab, L.iota, L.kc, L.vc);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(n_kv, BH), dim3(kThreads), 0, s, L.K, L.V, L.sel,
-                       L.N, L.n_src, L.k, L.kv_tab, L.iota, L.kc, L.vc);
+                       grid, L.k, L.kv_tab, L.iota, L.kc, L.vc);
   ISA_CHECK(hipGetLastError());
+
+  // General blocks (a partial block, or b != 64): 64-row tiles of 32-row
+  // slices; otherwise a tile is a block.
+  const bool gen = L.block != kBlock || (L.L_src % kBlock) != 0 || ((L.N - L.L_src) % kBlock) != 0;
+  const int shift = L.block == 32 ? 0 : L.block == 64 ? 1 : 2;
+  auto tiles = [&](int n_blocks) { return ((n_blocks << shift) + 1) / 2; };
+  const int key_tiles = gen ? tiles(n_kv) : n_kv;
+  const int flat_tiles = gen ? tiles(L.n_flat) : L.n_flat;
+  const int sharp_tiles = gen ? tiles(L.n_sharp) : L.n_sharp;
 
   BwdParams p;
   memset(&p, 0, sizeof(p));
@@ -902,6 +1068,11 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
   p.dk = L.dK;
   p.dv = L.dV;
   p.dkc_head_stride = (int64_t)n_kv * D;
+  p.grid = grid;
+  p.shift = shift;
+  p.kv_slices = n_kv << shift;
+  p.kvb_tab = L.kv_tab;
+  p.n_kv = n_kv;
 
   // block mask inside flat rows: tables of the exact blocks per flat block
   const bool masked = L.n_ns > 0 && L.n_flat > 0;
@@ -924,8 +1095,6 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
     p.tok_cap = 2 * L.n_ns;
     p.k_tok = L.K;
     p.v_tok = L.V;
-    p.kvb_tab = L.kv_tab;
-    p.n_kv = n_kv;
     p.tok_head_stride = (int64_t)L.N * D;
     p.fq_off = L.fq_off;
     p.fq_list = L.fq_list;
@@ -939,63 +1108,43 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
   pt.v = L.vc;
   pt.kv_rows = n_kv;
   pt.kv_head_stride = (int64_t)n_kv * D;
-  pt.lse_offset = (float)log((double)kBlock);
+  pt.lse_offset = (float)log((double)L.block);
   pt.q_tab = L.flat;
   pt.q_tab_stride = L.n_flat;
-  pt.n_q_entries = L.n_flat;
+  pt.n_q_entries = flat_tiles;
+  pt.q_slices = L.n_flat << shift;
   // keys = pooled rows t of this head's compact K^c_new: an identity row table
   pt.kv_tab = L.iota;
   pt.kv_tab_stride = 0;
   pt.dkc = L.dkc;
   pt.dvc = L.dvc;
-  if (L.n_flat > 0) {
-    const int kg = (n_kv + 127) / 128, qg = (L.n_flat + 1) / 2;
-    if (D == 128) {
-      ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<128, true, true>, kg, BH, pt, s, kT16)
-                       : launch_xcd(attn_bwd_dkdv16_kernel<128, true>, kg, BH, pt, s, kT16));
-      ISA_CHECK(masked ? launch_xcd(attn_bwd_dq16_kernel<128, true, true>, qg, BH, pt, s, kT16)
-                       : launch_xcd(attn_bwd_dq16_kernel<128, true>, qg, BH, pt, s, kT16));
-    } else {
-      ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<64, true, true>, kg, BH, pt, s, kT16)
-                       : launch_xcd(attn_bwd_dkdv16_kernel<64, true>, kg, BH, pt, s, kT16));
-      ISA_CHECK(masked ? launch_xcd(attn_bwd_dq16_kernel<64, true, true>, qg, BH, pt, s, kT16)
-                       : launch_xcd(attn_bwd_dq16_kernel<64, true>, qg, BH, pt, s, kT16));
-    }
-  }
 
   // exact path (sharp query blocks against K_new through the block table;
   // with the mask, then the flat blocks that take these keys token by token)
   BwdParams pe = p;
   pe.k = L.K;
   pe.v = L.V;
-  pe.kv_rows = n_kv * kBlock;
+  pe.kv_rows = key_tiles * kBN;
   pe.kv_head_stride = (int64_t)L.N * D;
   pe.lse_offset = 0.0f;
   pe.q_tab = L.sharp;
   pe.q_tab_stride = L.n_sharp;
-  pe.n_q_entries = L.n_sharp;
+  pe.n_q_entries = sharp_tiles;
+  pe.q_slices = L.n_sharp << shift;
   pe.dkc_in = L.n_flat > 0 ? L.dkc : nullptr;
   pe.dvc_in = L.n_flat > 0 ? L.dvc : nullptr;
-  pe.inv_w = 1.0f / (float)kBlock;
-  const int eg = (n_kv * kBlock + 127) / 128, sg = (L.n_sharp + 1) / 2;
-  if (D == 128) {
-    ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<128, false, true>, eg, BH, pe, s, kT16)
-                     : launch_xcd(attn_bwd_dkdv16_kernel<128, false>, eg, BH, pe, s, kT16));
-    if (L.n_sharp > 0)
-      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<128, false>, sg, BH, pe, s, kT16));
-  } else {
-    ISA_CHECK(masked ? launch_xcd(attn_bwd_dkdv16_kernel<64, false, true>, eg, BH, pe, s, kT16)
-                     : launch_xcd(attn_bwd_dkdv16_kernel<64, false>, eg, BH, pe, s, kT16));
-    if (L.n_sharp > 0)
-      ISA_CHECK(launch_xcd(attn_bwd_dq16_kernel<64, false>, sg, BH, pe, s, kT16));
-  }
+  pe.inv_w = 1.0f / (float)L.block;
+
+  auto paths = D == 128 ? (gen ? launch_paths<128, true> : launch_paths<128, false>)
+                        : (gen ? launch_paths<64, true> : launch_paths<64, false>);
+  ISA_CHECK(paths(pt, pe, masked, flat_tiles, sharp_tiles, n_kv, key_tiles, BH, s));
   if (L.n_ctx > 0) {
     if (D == 128)
       hipLaunchKernelGGL(bwd_zero_unselected_kernel<128>, dim3(L.n_ctx, BH), dim3(kThreads), 0, s,
-                         L.sel, L.N, L.L_src, L.k, L.dK, L.dV);
+                         L.sel, grid, L.k, L.dK, L.dV);
     else
       hipLaunchKernelGGL(bwd_zero_unselected_kernel<64>, dim3(L.n_ctx, BH), dim3(kThreads), 0, s,
-                         L.sel, L.N, L.L_src, L.k, L.dK, L.dV);
+                         L.sel, grid, L.k, L.dK, L.dV);
     ISA_CHECK(hipGetLastError());
   }
 #undef ISA_CHECK

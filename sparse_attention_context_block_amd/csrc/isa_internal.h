@@ -230,6 +230,7 @@ hipError_t launch_gather(const void* K, const void* V, const int32_t* sel, isa_d
 // [BH*(n_src+k)*D] bf16 (means of the kept blocks), dkc/dvc same shape f32.
 struct BwdLaunch {
   int BH, D, N, L_src, n_src, n_ctx, k, n_flat, n_sharp;
+  int block;  // b (32, 64 or 128); partial blocks allowed
   const bf16_bits *Q, *K, *V, *O, *dO;
   const float* lse;
   const int32_t *sel, *flat, *sharp;

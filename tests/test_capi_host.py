@@ -161,16 +161,23 @@ def test_partial_blocks_grid(L_src, L_ctx):
     assert p.info["n_flat"] == orc.flat_count(0.5, len(starts))
 
 
-def test_unaligned_gather_and_backward_unsupported():
+def test_unaligned_gather_unsupported_backward_checks_its_workspace():
+    # isa_gather needs whole blocks (K_new's length would depend on sel); the
+    # backward takes partial blocks and b = 32, 128, and refuses too small a
+    # workspace before any launch
     lib = isa._lib()
     p = isa.isa_plan_create(1, 2, 100, 200, 128, 64, 0.5, 0.5)
     fake = ctypes.c_void_p(0x1000)
     assert lib.isa_gather(p.handle, fake, fake, fake, fake, fake, None) == isa.ISA_ERR_UNSUPPORTED
     a = isa.isa_aux_t()
     a.sel = a.flat = a.sharp = 0x1000
-    st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
-                          fake, fake, fake, fake, 1 << 40, None)
-    assert st == isa.ISA_ERR_UNSUPPORTED
+    for b, (L_src, L_ctx) in ((64, (100, 200)), (32, (100, 200)), (128, (300, 500))):
+        p = isa.isa_plan_create(1, 2, L_src, L_ctx, 128, b, 0.5, 0.5)
+        need = lib.isa_backward_workspace_bytes(p.handle)
+        assert need > 0
+        st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
+                              fake, fake, fake, fake, need - 1, None)
+        assert st == isa.ISA_ERR_WORKSPACE
 
 
 def test_backward_with_block_mask_needs_ns():
@@ -256,13 +263,15 @@ def test_other_block_lengths_follow_the_oracle_counts(block, L_src, L_ctx):
     assert q.info["n_flat"] == 0
 
 
-def test_backward_needs_64_token_blocks():
+def test_backward_needs_bf16():
+    # the backward kernels take bf16 operands; an fp32 plan is refused before
+    # any launch, at every block length
     lib = isa._lib()
     fake = ctypes.c_void_p(0x1000)
     a = isa.isa_aux_t()
     a.sel = a.flat = a.sharp = 0x1000
-    for block in (32, 128):
-        p = isa.isa_plan_create(1, 2, 512, 512, 128, block, 0.5, 0.5)
+    for block in (32, 64, 128):
+        p = isa.isa_plan_create(1, 2, 512, 512, 128, block, 0.5, 0.5, dtype=isa.ISA_DTYPE_FP32)
         st = lib.isa_backward(p.handle, fake, fake, fake, fake, fake, fake, ctypes.byref(a),
                               fake, fake, fake, fake, 1 << 40, None)
         assert st == isa.ISA_ERR_UNSUPPORTED

@@ -28,8 +28,8 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f, alpha_ns=0.0):
-    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, 64, alpha_s, alpha_f, alpha_ns)
+def _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f, alpha_ns=0.0, block=64):
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, block, alpha_s, alpha_f, alpha_ns)
     q, k, v, do = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v", "do"))
     o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
     dq, dk, dv = isa.isa_backward(plan, q, k, v, o, do, lse, aux)
@@ -96,6 +96,37 @@ def test_backward_block_mask_parity(B, H, L_src, L_ctx, D, alpha_s, alpha_f, alp
             for j in range(L_ctx // 64):
                 if j not in aux["sel"][bi, h]:
                     assert not dk[bi, h, L_src + 64 * j:L_src + 64 * (j + 1)].any()
+
+
+@pytest.mark.parametrize("B,H,L_src,L_ctx,D,b,alpha_s,alpha_f,alpha_ns,seed", [
+    (1, 2, 1000, 1100, 128, 64, 0.5, 0.5, 0.0, 71),    # both segments end in a partial block
+    (1, 2, 40, 600, 128, 64, 0.5, 0.5, 0.0, 72),       # the source is one partial block
+    (1, 2, 512, 40, 128, 64, 1.0, 0.5, 0.0, 73),       # the context is one partial block, kept
+    (2, 2, 700, 900, 64, 64, 0.34, 0.3, 0.0, 74),      # D = 64, B = 2, partial blocks
+    (1, 2, 512, 512, 128, 32, 0.5, 0.5, 0.0, 75),      # b = 32: two blocks per tile
+    (1, 3, 500, 300, 64, 32, 0.34, 0.45, 0.0, 76),     # b = 32, partial, odd block counts
+    (1, 2, 1024, 1024, 128, 128, 0.5, 0.5, 0.0, 77),   # b = 128: two tiles per block
+    (2, 2, 700, 900, 64, 128, 0.5, 0.3, 0.0, 78),      # b = 128, partial (one-tile blocks)
+    (1, 2, 1000, 1100, 128, 64, 0.5, 0.5, 0.125, 79),  # partial blocks with the block mask
+])
+def test_backward_general_blocks_parity(B, H, L_src, L_ctx, D, b, alpha_s, alpha_f, alpha_ns,
+                                        seed):
+    """Partial blocks (either segment not a multiple of b) and b = 32, 128: the
+    GPU backward against isa_ref_bwd on the same grid."""
+    _say(f"bwd blocks B{B} H{H} L_src{L_src} L_ctx{L_ctx} D{D} b{b} as{alpha_s} af{alpha_f} "
+         f"ans{alpha_ns} seed{seed}")
+    inp = generate(B, H, L_src, L_ctx, D, b, seed=seed, variant="icl", grad=True)
+    plan, grads, aux = _fwd_bwd(inp, B, H, L_src, L_ctx, D, alpha_s, alpha_f, alpha_ns, b)
+    ref = orc.isa_ref_bwd(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v", "do")),
+                          L_src, L_ctx, b, aux["sel"], aux["flat"], aux.get("ns"))
+    _check_grads([out_f64(g) for g in grads], ref, "blocks")
+    starts, ends, n_src, n_ctx = orc.block_grid(L_src, L_ctx, b)
+    dk = out_f64(grads[1])
+    for bi in range(B):
+        for h in range(H):
+            for j in range(n_ctx):
+                if j not in aux["sel"][bi, h]:
+                    assert not dk[bi, h, starts[n_src + j]:ends[n_src + j]].any()
 
 
 def test_backward_block_mask_deterministic():

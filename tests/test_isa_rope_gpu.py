@@ -149,27 +149,32 @@ def test_rope_workload_scale():
             heads=[(0, 1), (0, 3)])
 
 
-@pytest.mark.parametrize("B,H,L_src,L_ctx,D,alpha_s,alpha_f,base,seed", [
-    (1, 2, 512, 512, 128, 0.5, 0.5, 10000.0, 81),
-    (1, 3, 640, 448, 128, 0.25, 0.5, 100.0, 82),   # 17 blocks, a fast-turning base
-    (2, 2, 1024, 768, 64, 0.34, 0.3, 10000.0, 83),  # D = 64, B = 2
+@pytest.mark.parametrize("B,H,L_src,L_ctx,D,alpha_s,alpha_f,base,seed,b,alpha_ns", [
+    (1, 2, 512, 512, 128, 0.5, 0.5, 10000.0, 81, 64, 0.0),
+    (1, 3, 640, 448, 128, 0.25, 0.5, 100.0, 82, 64, 0.0),   # 17 blocks, a fast-turning base
+    (2, 2, 1024, 768, 64, 0.34, 0.3, 10000.0, 83, 64, 0.0),  # D = 64, B = 2
+    (1, 2, 1000, 600, 128, 0.5, 0.5, 10000.0, 84, 64, 0.0),  # partial blocks
+    (1, 2, 1024, 1024, 128, 0.5, 0.5, 10000.0, 85, 128, 0.0),  # b = 128
+    (1, 2, 1024, 1024, 128, 0.5, 0.5, 10000.0, 86, 64, 0.0625),  # with the block mask
 ])
-def test_rope_backward_parity(B, H, L_src, L_ctx, D, alpha_s, alpha_f, base, seed):
+def test_rope_backward_parity(B, H, L_src, L_ctx, D, alpha_s, alpha_f, base, seed, b, alpha_ns):
     """The decision-frozen backward with the rotary embedding against the
     oracle's isa_ref_bwd_rope (the backward at the rotated inputs, dQ and dK
     turned back).  Bars as the other backward tests: relative Frobenius <= 1e-2
     and max-abs <= 2e-2 of the largest reference magnitude per tensor."""
     _say(f"rope bwd B{B} H{H} L_src{L_src} L_ctx{L_ctx} D{D} as{alpha_s} af{alpha_f} "
          f"base{base} seed{seed}")
-    inp = generate(B, H, L_src, L_ctx, D, 64, seed=seed, variant="icl", grad=True)
-    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, 64, alpha_s, alpha_f, rope_base=base)
+    inp = generate(B, H, L_src, L_ctx, D, b, seed=seed, variant="icl", grad=True)
+    plan = isa.isa_plan_create(B, H, L_src, L_ctx, D, b, alpha_s, alpha_f, alpha_ns,
+                               rope_base=base)
     q, k, v, do = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v", "do"))
     o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
     dq, dk, dv = isa.isa_backward(plan, q, k, v, o, do, lse, aux)
     torch.cuda.synchronize()
     sel, flat = aux["sel"].cpu().numpy(), aux["flat"].cpu().numpy()
+    ns = aux["ns"].cpu().numpy() if "ns" in aux else None
     ref = orc.isa_ref_bwd_rope(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v", "do")),
-                               L_src, L_ctx, 64, sel, flat, base, "bf16")
+                               L_src, L_ctx, b, sel, flat, base, "bf16", ns)
     for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         g = out_f64(g)
         rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
