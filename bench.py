@@ -247,13 +247,60 @@ def _short(name):
     return name.split("(")[0]
 
 
-def summarize(paths):
-    """Summarise rocprofv3 CSVs per (kernel, grid): kernel traces give the
-    average duration; counter collections give the average value per dispatch
-    of every counter.  Prints a text table."""
+def sq_derived(paths):
+    """Derived SQ metrics per (kernel, grid) over the counter CSVs together:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over SQ_CYCLES / 32 (the
+    chip's 32 SQ_CYCLES counters are summed); coexec = SQ_VALU_MFMA_COEXEC_CYCLES
+    over SQ_VALU_MFMA_BUSY_CYCLES; issue, wait_inst, wait_any = SQ_ACTIVE_INST_ANY,
+    SQ_WAIT_INST_ANY, SQ_WAIT_ANY over SQ_WAVE_CYCLES; insts/wave = SQ_INSTS over
+    the grid's waves.  Returns the table as text ("" without SQ counters)."""
     import csv
     from collections import defaultdict
 
+    acc = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if "Counter_Name" not in r or not r["Counter_Name"].startswith("SQ_"):
+                continue
+            acc[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+                float(r["Counter_Value"]))
+    if not acc:
+        return ""
+    pct = lambda x: f"{x:.1%}" if x is not None else "-"
+    lines = [f"{'kernel':52s} {'grid':>8s} {'waves':>7s} {'MFMA busy':>9s} {'coexec':>7s} "
+             f"{'issue':>6s} {'wait_inst':>9s} {'wait_any':>8s} {'insts/wave':>10s} "
+             f"{'LDS confl':>10s}"]
+    for (k, g), cs in sorted(acc.items()):
+        if k.startswith("at::"):
+            continue
+        c = {n: float(np.mean(v)) for n, v in cs.items()}
+        waves = g / 64
+        cyc, busy, wc = c.get("SQ_CYCLES"), c.get("SQ_VALU_MFMA_BUSY_CYCLES"), c.get("SQ_WAVE_CYCLES")
+        mb = busy / 1024 / (cyc / 32) if busy is not None and cyc else None
+        co = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy if busy and "SQ_VALU_MFMA_COEXEC_CYCLES" in c \
+            else None
+        per_wave = lambda n: c[n] / wc if wc and n in c else None
+        ipw = int(c["SQ_INSTS"] / waves) if "SQ_INSTS" in c else "-"
+        lc = int(c["SQ_LDS_BANK_CONFLICT"]) if "SQ_LDS_BANK_CONFLICT" in c else "-"
+        lines.append(f"{k[:52]:52s} {g:8d} {int(waves):7d} {pct(mb):>9s} {pct(co):>7s} "
+                     f"{pct(per_wave('SQ_ACTIVE_INST_ANY')):>6s} "
+                     f"{pct(per_wave('SQ_WAIT_INST_ANY')):>9s} "
+                     f"{pct(per_wave('SQ_WAIT_ANY')):>8s} {ipw:>10} {lc:>10}")
+    return "\n".join(lines)
+
+
+def summarize(paths):
+    """Summarise rocprofv3 CSVs per (kernel, grid): kernel traces give the
+    average duration; counter collections give the average value per dispatch
+    of every counter (and, with SQ counters, the derived table of sq_derived
+    first).  Prints a text table."""
+    import csv
+    from collections import defaultdict
+
+    derived = sq_derived(paths)
+    if derived:
+        print(derived)
+        print()
     for path in paths:
         rows = list(csv.DictReader(open(path)))
         print(f"# {path}")
