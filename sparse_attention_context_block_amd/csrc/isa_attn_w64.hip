@@ -28,14 +28,27 @@
 //
 // Software pipeline of one wave over key tile t: 64 MFMA slots of one product
 // each, O += V(t-1) P(t-1) in slots 0-31 and S(t+1) = K(t+1) Q^T in slots
-// 32-63, with the softmax of tile t (and the end of tile t-1's) issued between
-// the products, about one exponential per slot.  S is double-buffered (the
-// scores of tiles t and t+1 live in two register sets), so the exponentials of
-// a tile run on while the next tile's products fill the other set.  A single
-// wave issues in order, so the schedule is written out slot by slot (the table
-// above the loop) and fenced, which keeps the compiler from regrouping it.
-// Each iteration ends at a barrier: tile t+2 has landed, and every wave is done
-// with V(t-1) and K(t+1), whose ring slots the next iteration's loads reuse.
+// 32-63, with the softmax of tile t issued between the products, one
+// exponential per slot.  S is double-buffered (the scores of tiles t and t+1
+// live in two register sets), so the exponentials of a tile run on while the
+// next tile's products fill the other set.  A single wave issues in order, so
+// the schedule is written out slot by slot (the table above the loop) and
+// fenced, which keeps the compiler from regrouping it.  Each iteration ends at
+// a barrier: tile t+2 has landed, and every wave is done with V(t-1) and
+// K(t+1), whose ring slots the next iteration's loads reuse.
+//
+// Softmax reference: a wave issues one instruction at a time and a product
+// hides only about half of its own 32 cycles of other work, so the per-tile
+// row maxima of the online softmax (32 max3 and a cross-lane decision per
+// tile) are not taken.  Each tile is exponentiated against a running
+// reference, first the row maxima of tile 0; its row sums, complete before
+// any product reads the tile's weights, show whether that was safe.  A sum
+// above 2^8 raises the reference by its next power of two (O and l rescaled
+// exactly; the tile's own sum is taken over the bf16 weights the products
+// use).  A sum above 2^64 or not finite means the weights may have
+// overflowed: the workgroup writes a NaN mark into its first output, and a
+// second launch of this kernel recomputes the marked workgroups from the exact
+// row maxima (every other workgroup of that launch reads its mark and exits).
 //
 // The products are inline asm, whose latency the compiler does not know: every
 // read of their results is placed a product or an explicit wait after them, no
@@ -68,7 +81,11 @@ constexpr int kNK = 3, kNV = 5;               // ring slots
 constexpr int kVBase = kNK * kKTile;          // V ring after the K ring
 constexpr int kLds = kVBase + kNV * kVTile;   // 154624 bytes
 constexpr int kKSlots = kBN * (kKStride / 16);  // 1088 16-byte slots per K tile
-constexpr float kRescaleThreshold = 8.0f;     // log2 units
+// A tile's row sum against the current reference above kRebase raises the
+// reference; above kOverflow (or not finite) its exponentials may have
+// overflowed and the workgroup is marked.
+constexpr float kRebase = 256.0f;
+constexpr float kOverflow = 18446744073709551616.0f;  // 2^64
 static_assert(kKSlots <= 17 * 64 && kBN * (kVStride / 16) == 20 * 64, "DMA split");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -157,7 +174,10 @@ __device__ __forceinline__ float max2(float a, float b) {
 // kPartial: some key tiles may hold fewer than 64 valid rows (plans whose
 // source or context length is not a multiple of b); without it every tile is
 // whole, and the loop carries no masking or clamping code.
-template <int kShift, bool kPartial>
+// kFixup: the second launch, which recomputes (from the exact row maxima) the
+// workgroups whose exponentials the first one found overflowed; the others
+// exit at once.
+template <int kShift, bool kPartial, bool kFixup>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p) {
   static_assert(kShift == 1 || kShift == 2, "a key tile is 64 rows of one block");
   constexpr int D = kD;
@@ -183,6 +203,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
   const int e = qt * 4 + wave;
   const bool wave_valid = e < p.n_q_entries;
   const int32_t* qlist = p.q_tab ? p.q_tab + bh * p.q_tab_stride : nullptr;
+  if constexpr (kFixup) {
+    // the first launch's mark: dim 0 of row 0 of wave 0's first half; not NaN:
+    // the whole workgroup exits before loading anything else
+    const Slice q0 = list_slice(p.grid, qlist, p.n_q_slices, kShift, 2 * (qt * 4));
+    const bf16_bits mark =
+        *(static_cast<const bf16_bits*>(p.o) + bh * p.q_head_stride + (int64_t)q0.start * D);
+    if (!((mark & 0x7f80u) == 0x7f80u && (mark & 0x7fu) != 0)) return;
+  }
   const bf16_bits* Qh = static_cast<const bf16_bits*>(p.q) + bh * p.q_head_stride;
   bool q_ok[2];
   int64_t qrow[2];
@@ -331,9 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[h][j][r] = 0.0f;
-  // S^T of two consecutive tiles: [tile parity][half][key subtile].  The
-  // second set is zero before tile 0, so the first iteration's work on "tile
-  // -1" (below) yields exact zeros.
+  // S^T of two consecutive tiles: [tile parity][half][key subtile]
   f32x16_t sacc[2][2][2];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -350,15 +376,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int e2 = 0; e2 < 8; ++e2) pk[h][c][e2] = (__bf16)0.0f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  // -m of the tile whose exponentials use it, by tile parity (-inf for "tile
-  // -1": its exponentials are 0)
-  float mneg[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+  // Reference of O and l per half (scaled log2 units) and its negative, which
+  // the exponentials add.  A tile is exponentiated against the current
+  // reference, not against its own row max, and the row sums of its
+  // exponentials, complete before any product reads them, show whether that
+  // was safe: a sum above kRebase (or not finite) sends the tile down the rare
+  // path, which takes its exact row maxima, raises the reference, redoes its
+  // exponentials and rescales O and l.
+  float m_run[2], mneg[2];
   float l_run[2] = {0.0f, 0.0f};
-  float tmax[2];       // running tile max (keys 0-31 first, then 32-63)
-  // exponentials of a pair: [pair & 1][element] (zero for the pairs of "tile
-  // -1" whose elements no iteration computed)
-  float pe[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  float l_tile[2] = {0.0f, 0.0f};  // this lane's part of the current tile's row sums
+  // a rebase at the end of tile t: O (which then still takes P(t) against the
+  // old reference) is rescaled after P(t)'s products, in slot 31 of the next
+  // iteration or at the end of the tail
+  float alpha[2] = {1.0f, 1.0f};
+  bool up[2] = {false, false};
+  bool dirty = false;  // a tile's row sum was not finite or above kOverflow
+  float m_init[2] = {0.0f, 0.0f};  // fix-up launch: the exact row maxima
+  __shared__ int vote[4];          // the waves' marks
+  // exponentials waiting for their pair's pack: element j at j & 7
+  float pe[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   float sl2 = p.scale_log2;
   asm("" : "+s"(sl2));
 
@@ -368,31 +405,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
   // 8 (c & 1) + e2 of S^T subtile c >> 1.
   auto elem = [&](int par, int j) __attribute__((always_inline)) {
     const int pr = j >> 1, c = pr >> 3, h = (pr >> 2) & 1, e2 = 2 * (pr & 3) + (j & 1);
-    pe[pr & 1][j & 1] =
-        __builtin_amdgcn_exp2f(fmaf(sacc[par][h][c >> 1][8 * (c & 1) + e2], sl2, mneg[par][h]));
-    anchor(pe[pr & 1][j & 1]);
+    pe[j & 7] =
+        __builtin_amdgcn_exp2f(fmaf(sacc[par][h][c >> 1][8 * (c & 1) + e2], sl2, mneg[h]));
+    anchor(pe[j & 7]);
   };
-  // Pair p into P^T (bf16, round to nearest even) and into the row sum, which
-  // adds the fp32 exponentials: v_dot2c_f32_bf16 on the packed pair issues on
-  // the matrix pipe and would wait for the product in flight.
+  // Pair p into P^T (bf16, round to nearest even) and into the tile's row sum,
+  // which adds the fp32 exponentials: v_dot2c_f32_bf16 on the packed pair
+  // issues on the matrix pipe and would wait for the product in flight.
+  // Pairs 0 and 4 are the first of their half in a tile.
   auto pack = [&](int pr) __attribute__((always_inline)) {
     const int c = pr >> 3, h = (pr >> 2) & 1, e2 = 2 * (pr & 3);
-    pk[h][c][e2] = (__bf16)pe[pr & 1][0];
-    pk[h][c][e2 + 1] = (__bf16)pe[pr & 1][1];
+    const float a0 = pe[(2 * pr) & 7], a1 = pe[(2 * pr + 1) & 7];
+    pk[h][c][e2] = (__bf16)a0;
+    pk[h][c][e2 + 1] = (__bf16)a1;
     // (the packed pair is used only by the next tile's products: without the
     // anchor the compiler sinks the conversion out of its slot, to the start
     // of the next iteration, where no product is in flight to hide it)
     anchor(__uint_as_float(__builtin_bit_cast(u32x4, pk[h][c])[pr & 3]));
-    l_run[h] = (l_run[h] + pe[pr & 1][0]) + pe[pr & 1][1];
-    anchor(l_run[h]);
+    if (pr == 0 || pr == 4)
+      l_tile[h] = a0 + a1;
+    else
+      l_tile[h] = (l_tile[h] + a0) + a1;
+    anchor(l_tile[h]);
   };
-  // tmax[h] = max(tmax[h], values 2 i .. 2 i + 1 of subtile s) for both halves
-  auto max_step = [&](int par, int s, int i) __attribute__((always_inline)) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      tmax[h] = fmaxf(fmaxf(tmax[h], sacc[par][h][s][2 * i]), sacc[par][h][s][2 * i + 1]);
-      anchor(tmax[h]);
-    }
+  // slot of the pack of pair p: chunk 0's pairs wait for slot 8 (P(t-1) chunk 0
+  // is read in slots 0-7), the others follow their elements by one slot
+  auto pack_slot = [](int pr) constexpr -> int {
+    return pr < 4 ? 8 + pr : (pr < 7 ? 2 * pr + 4 - (pr - 4) : 2 * pr + 2);
   };
   // keys >= cnt of subtile s get -inf (partial tiles only)
   auto mask_subtile = [&](int par, int s, int cnt) __attribute__((always_inline)) {
@@ -407,65 +446,103 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
         }
     }
   };
-
-  // ---- prologue: tiles 0-2 requested, 0 and 1 landed; S(0) ----
-  // The first iteration's O += V(-1) P(-1) reads V slot kNV - 1 with P = 0:
-  // zero that slot so the product is exactly 0.
-  {
-    lds_u4* z = (lds_u4*)(uintptr_t)(lds0 + kVBase + (kNV - 1) * kVTile);
+  // the row maxima of S^T set par (both subtiles; the partner lane holds the
+  // other 32 keys of the row), in scaled log2 units
+  auto row_max = [&](int par, float (&mx)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kVTile / 16 / kThreads; ++i) z[tid + kThreads * i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  // block ids of the tiles the loop requests next (t + 3) and masks (t + 1)
-  int id_t3 = tile_id(3);
-  int id_t1 = tile_id(1), id_t2 = tile_id(2);
-  dma_tile(tile_id(0), 0);
-  dma_tile(id_t1, 1);
-  dma_tile(id_t2, 2);
-  ISA_WAIT_ALL_BUT_LAST_TILE();
-  __syncthreads();  // (also publishes the zeroed slot)
-  int cnt_cur = tile_of(tile_id(0), 0).cnt;
-  {
-    bf16x8_t kf[16];
-    const uint32_t k0 = lane_addr(k_lane, 0);
-    kf[0] = k_frag(k0, 0);
-    kf[1] = k_frag(k0, 1);
+    for (int h = 0; h < 2; ++h) {
+      float t = sacc[par][h][0][0];
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      if (f + 2 < 16) kf[f + 2] = k_frag(k0, f + 2);
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) mfma_qk(sacc[0][h][f >> 3], kf[f], qreg[h][f & 7], (f & 7) == 0);
+        for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[par][h][s2][r]);
+      const uint32_t u = __float_as_uint(t);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      mx[h] = max2(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
     }
-    wait_s(sacc[0]);  // S(0) is read next by VALU
-    mask_subtile(0, 0, cnt_cur);
+  };
+  // Tile t fully exponentiated and packed: fold its row sums into l.  Rare: a
+  // sum above kRebase.  Then the reference rises by the next power of two of
+  // the sum (so P(t) against the new one is at most 1), l is rescaled here and O
+  // after P(t)'s products (slot 31 of the next iteration, or the tail).  A sum
+  // above kOverflow (or not finite) means P(t) may hold infinities: the
+  // workgroup is marked for the fix-up launch.
+  auto check_tile = [&]() __attribute__((always_inline)) {
+    const bool any =
+        __builtin_amdgcn_ballot_w64(!(max2(l_tile[0], l_tile[1]) <= kRebase)) != 0;
+    fence();
+    if (any) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) tmax[h] = -INFINITY;
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t u = __float_as_uint(l_tile[h]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        const float L = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // the row's sum
+        const bool big = !(L <= kRebase);
+        dirty = dirty || !(L <= kOverflow);
+        // A rebased row's sum is taken again over the packed bf16 weights the
+        // products use, so that numerator and denominator hold the same
+        // weights: its largest weight, which dominates the row, is not 1 here.
+        float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) max_step(0, 0, i);
-  }
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) part += (float)pk[h][c][e2];
+        const float lt = big ? part : l_tile[h];
+        const uint32_t w = __float_as_uint(lt);
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+        const float L2 = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+        const float k = big ? ceilf(__builtin_amdgcn_logf(L2)) : 0.0f;
+        alpha[h] = __builtin_amdgcn_exp2f(-k);  // a power of two: exact
+        m_run[h] += k;
+        mneg[h] = -m_run[h];
+        up[h] = __builtin_amdgcn_ballot_w64(big) != 0;
+        l_run[h] = (l_run[h] + lt) * alpha[h];
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        l_run[h] += l_tile[h];
+        up[h] = false;
+      }
+    }
+    fence();
+  };
+  // O *= alpha after a rebase (rare), once the products that read O are done
+  auto rescale_o = [&]() __attribute__((always_inline)) {
+    fence();
+    if (up[0] || up[1]) {
+      wait_o(oacc);  // the accumulating products finish before O is read
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[h][j][r] *= alpha[h];
+      wait_o(oacc);  // and the writes land before the next product reads O
+    }
+  };
+
+  // block ids of the tiles the loop requests next (t + 3) and masks (t + 1),
+  // and the valid rows of the current tile
+  int id_t1 = 0, id_t2 = 0, id_t3 = 0, cnt_cur = 0;
 
   // ---- the tile loop: 64 MFMA slots per tile, one product each ----
   //   slots  0-31  O += V(t-1) P(t-1): slot i is fragment i >> 1, half i & 1
   //   slots 32-63  S(t+1) = K(t+1) Q^T: slot 32 + i is fragment i >> 1, half i & 1
   //                (into the other S set: S(t) stays until its exponentials end)
-  // VALU work placed after the products, spread so that each slot's work fits
-  // the 32 cycles of its product (in-order issue makes a second product wait
-  // for the first; work that does not fit delays the next product):
-  //   every slot    one exponential: tile t's element slot - 20 in slots 20-63,
-  //                 tile t-1's element slot + 44 in slots 0-19
-  //   even slots    pack + row sum of a pair two slots after its elements:
-  //                 tile t's pair (slot - 22) / 2 in slots 22-62, tile t-1's pair
-  //                 (slot + 42) / 2 in slots 0-20.  Chunk c of P(t) is packed
-  //                 in slots 22 + 16 c .. 36 + 16 c (mod 64): after P(t-1) chunk c
-  //                 was last read (slot 8 c + 7) and before P(t) chunk c is read
-  //                 (slot 8 c of the next tile)
-  //   odd slots 1-15   row max over keys 32-63 of S(t) (keys 0-31 were done in
-  //                    the previous tile's odd slots 49-63, after their last
-  //                    product in slot 47)
-  //   slots 16-21   running max and rescale decision, a dependent chain: swap
-  //                 with the partner lane, one half per slot; compare and
-  //                 ballot; new max; 2^(old - new); and, after tile t-1's last
-  //                 pair and before tile t's first, l *= alpha (slot 21)
+  // VALU work placed after the products (packs before exponentials), spread so
+  // that each slot's work fits the 32 cycles of its product (in-order issue
+  // makes a second product wait for the first; work that does not fit delays
+  // the next product):
+  //   every slot    one exponential of tile t: element = slot (subtile 0, keys
+  //                 0-31, in slots 0-31; its products ended in the previous
+  //                 iteration's slot 47; subtile 1 from slot 32)
+  //   packs         pair p (elements 2p, 2p + 1) of tile t: chunk 0 (pairs 0-7)
+  //                 in slots 8-16, after P(t-1) chunk 0 was last read (slot 7);
+  //                 pair p >= 7 in slot 2p + 2 (chunk c from slot 16c + 2, after
+  //                 P(t-1) chunk c was last read in slot 8c + 7); pair 31 after
+  //                 slot 63
+  //   after slot 63  tile t's row sums checked and folded into l (rare: rebase)
   //   odd slots 21-39  loads of tile t + 3, one per slot (into the ring slots
   //                 of K(t) and V(t-2), which no wave reads after the last barrier)
   // Fragment reads run three fragments (six slots) ahead of their products.
@@ -478,14 +555,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     const int cnt_next = tile_of(id_t1, min(t + 1, n_tiles - 1)).cnt;
     const uint32_t vprev = lane_addr(v_lane, kVBase + ((t + kNV - 1) % kNV) * kVTile);
     const uint32_t knext = lane_addr(k_lane, ((t + 1) % kNK) * kKTile);
-    mask_subtile(P, 1, cnt_cur);
     bf16x8_t vf[16], kf[16];
     vf[0] = v_frag(vprev, 0);
     vf[1] = v_frag(vprev, 1);
     vf[2] = v_frag(vprev, 2);
     fence();
-    float alpha[2], ts[2], dm[2];
-    bool up[2];
     static_for<0, 64>([&](auto slot_c) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
       // ---- fragment reads, three fragments ahead ----
@@ -502,79 +576,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
         mfma_qk(sacc[Q][h][f >> 3], kf[f], qreg[h][f & 7], (f & 7) == 0);
       }
       // ---- VALU work of this slot ----
-      if constexpr (slot <= 20 && (slot & 1) == 0) pack((slot + 42) >> 1);  // tile t-1
-      if constexpr (slot >= 22 && (slot & 1) == 0) pack((slot - 22) >> 1);  // tile t
-      if constexpr (slot < 20) elem(Q, slot + 44);                          // tile t-1
-      if constexpr (slot >= 20) elem(P, slot - 20);                         // tile t
-      if constexpr (slot >= 1 && slot <= 15 && (slot & 1) == 1) max_step(P, 1, (slot - 1) >> 1);
-      // running max and rescale decision, spread over slots 16-21: the swap
-      // with the partner lane and the tile max of half 0 (16) and half 1 (17),
-      // the ballots (18), the new max (19), 2^(old - new) (20) and l *= alpha
-      // (21, after tile t-1's last pair and before tile t's first)
-      if constexpr (slot == 16 || slot == 17) {
-        constexpr int h = slot - 16;
-        // the swap returns {own, partner} in an order that depends on the
-        // half of the wave, so take both
-        const uint32_t u = __float_as_uint(tmax[h]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        ts[h] = max2(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
-        anchor(ts[h]);
-      }
-      if constexpr (slot == 18) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          up[h] = __builtin_amdgcn_ballot_w64(ts[h] > m_run[h] + kRescaleThreshold) != 0;
-      }
-      if constexpr (slot == 19) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float mx = max2(m_run[h], ts[h]);  // (unconditional: no branch)
-          const float m_new = up[h] ? mx : m_run[h];
-          dm[h] = m_run[h] - m_new;
-          m_run[h] = m_new;
-          mneg[P][h] = -m_new;
-          anchor(dm[h]);
-          anchor(mneg[P][h]);
-        }
-      }
-      if constexpr (slot == 20) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          alpha[h] = up[h] ? __builtin_amdgcn_exp2f(dm[h]) : 1.0f;
-          anchor(alpha[h]);
-        }
-      }
-      if constexpr (slot == 21) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          l_run[h] *= alpha[h];
-          anchor(l_run[h]);
-        }
-      }
-      if constexpr (slot == 31) {
-        fence();
-        // rare: the running max rose; O (with P(t-1) V(t-1) in it) *= alpha
-        if (up[0] || up[1]) {
-          wait_o(oacc);  // the accumulating products finish before O is read
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[h][j][r] *= alpha[h];
-          wait_o(oacc);  // and the writes land before the next product reads O
-        }
-      }
-      if constexpr (slot == 48) {
-        mask_subtile(Q, 0, cnt_next);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) tmax[h] = -INFINITY;
-      }
-      if constexpr (slot >= 49 && (slot & 1) == 1) max_step(Q, 0, (slot - 49) >> 1);
+      if constexpr (slot == 32) mask_subtile(P, 1, cnt_cur);  // (partial tiles)
+      static_for<0, 31>([&](auto pr_c) __attribute__((always_inline)) {
+        constexpr int pr = decltype(pr_c)::value;
+        if constexpr (pack_slot(pr) == slot) pack(pr);
+      });
+      elem(P, slot);
+      if constexpr (slot == 31) rescale_o();  // (rare) after P(t-1)'s products
+      if constexpr (slot == 48) mask_subtile(Q, 0, cnt_next);
       if constexpr (slot >= 21 && slot < 40 && (slot & 1) == 1)
         dma_issue(dma, std::integral_constant<int, ((slot - 21) >> 1)>{});
       fence();
     });
+    pack(31);
+    check_tile();
     cnt_cur = cnt_next;
     id_t1 = id_t2;
     id_t2 = id_t3;
@@ -597,12 +612,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
       asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
     }
   };
-  // ---- last tile: its remaining pairs and O += V(n-1) P(n-1) ----
+  // ---- last tile: O += V(n-1) P(n-1) ----
   // Ends with every product written: the caller's paths join after it, and a
   // register copy the compiler places at a join would otherwise read an
   // accumulator before its product (inline asm, of unknown latency) wrote it.
-  auto tail = [&](auto par_c) __attribute__((always_inline)) {
-    constexpr int Q = decltype(par_c)::value;  // parity of tile n - 1
+  auto tail = [&]() __attribute__((always_inline)) {
     // The paths into the tail may keep O in other registers; the copies the
     // compiler then places at the join must land before the first product
     // reads O (inline asm: the compiler inserts no wait states for it).
@@ -618,10 +632,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
         vf[(slot >> 1) + 3] = v_frag(vlast, (slot >> 1) + 3);
       constexpr int f = slot >> 1, h = slot & 1;
       mfma_pv(oacc[h][f & 3], vf[f], pk[h][f >> 2]);
-      if constexpr (slot <= 20 && (slot & 1) == 0) pack((slot + 42) >> 1);
-      if constexpr (slot < 20) elem(Q, slot + 44);
       fence();
     });
+    rescale_o();  // (rare) a rebase at the end of the last tile
     // drain the loads issued for tiles past the end before the workgroup exits
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     wait_o(oacc);
@@ -631,6 +644,86 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     keep_s(sacc[0]);
     keep_s(sacc[1]);
   };
+  // The exact row maxima over every key tile (K only, one tile at a time): the
+  // fix-up launch's reference for a workgroup the first launch marked.
+  auto exact_maxima = [&]() {
+    float tm[2] = {-INFINITY, -INFINITY};
+    for (int u = 0; u < n_tiles; ++u) {
+      const int blk = tile_id(u);
+      const Dma d = dma_plan(blk, u);
+      dma_issue(d, std::integral_constant<int, 0>{});
+      dma_issue(d, std::integral_constant<int, 1>{});
+      dma_issue(d, std::integral_constant<int, 2>{});
+      dma_issue(d, std::integral_constant<int, 3>{});
+      dma_issue(d, std::integral_constant<int, 9>{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const uint32_t kk0 = lane_addr(k_lane, (u % kNK) * kKTile);
+#pragma unroll
+      for (int f = 0; f < 16; ++f) {
+        const bf16x8_t kfr = k_frag(kk0, f);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) mfma_qk(sacc[0][h][f >> 3], kfr, qreg[h][f & 7], (f & 7) == 0);
+      }
+      wait_s(sacc[0]);
+      const int cnt = tile_of(blk, u).cnt;
+      mask_subtile(0, 0, cnt);
+      mask_subtile(0, 1, cnt);
+      float mx[2];
+      row_max(0, mx);
+      tm[0] = max2(tm[0], mx[0]);
+      tm[1] = max2(tm[1], mx[1]);
+      __syncthreads();  // every wave is done with the slot before it is reused
+    }
+    m_init[0] = tm[0];
+    m_init[1] = tm[1];
+  };
+
+  // The first launch takes tile 0's row maxima as the first reference; the
+  // fix-up launch, for the workgroups the first one marked, the exact row
+  // maxima over every tile, so that no tile can exceed its reference.
+  if constexpr (kFixup) exact_maxima();
+  // ---- prologue: tiles 0-2 requested, 0 and 1 landed; S(0) and the first
+  // reference (tile 0's exact row maxima) ----
+  // The first iteration's O += V(-1) P(-1) reads V slot kNV - 1 with P = 0:
+  // zero that slot so the product is exactly 0.
+  {
+    lds_u4* z = (lds_u4*)(uintptr_t)(lds0 + kVBase + (kNV - 1) * kVTile);
+#pragma unroll
+    for (int i = 0; i < kVTile / 16 / kThreads; ++i) z[tid + kThreads * i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  id_t3 = tile_id(3);
+  id_t1 = tile_id(1);
+  id_t2 = tile_id(2);
+  dma_tile(tile_id(0), 0);
+  dma_tile(id_t1, 1);
+  dma_tile(id_t2, 2);
+  ISA_WAIT_ALL_BUT_LAST_TILE();
+  __syncthreads();  // (also publishes the zeroed slot)
+  cnt_cur = tile_of(tile_id(0), 0).cnt;
+  {
+    bf16x8_t kf[16];
+    const uint32_t k0 = lane_addr(k_lane, 0);
+    kf[0] = k_frag(k0, 0);
+    kf[1] = k_frag(k0, 1);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      if (f + 2 < 16) kf[f + 2] = k_frag(k0, f + 2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) mfma_qk(sacc[0][h][f >> 3], kf[f], qreg[h][f & 7], (f & 7) == 0);
+    }
+    wait_s(sacc[0]);  // S(0) is read next by VALU
+    mask_subtile(0, 0, cnt_cur);
+    mask_subtile(0, 1, cnt_cur);
+    float mx[2];
+    row_max(0, mx);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      m_run[h] = kFixup ? m_init[h] : mx[h];
+      mneg[h] = -m_run[h];
+    }
+  }
+
   // Two iterations per trip (tile parity 0, then 1): the two copies of the
   // body alternate between the two S sets.
   int t = 0;
@@ -639,10 +732,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
     iteration(t + 1, std::integral_constant<int, 1>{});
   }
   if (t < n_tiles) iteration(t, std::integral_constant<int, 0>{});
-  if ((n_tiles - 1) & 1)
-    tail(std::integral_constant<int, 1>{});
-  else
-    tail(std::integral_constant<int, 0>{});
+  tail();
+
+  // the waves' marks: a marked workgroup is redone by the fix-up launch
+  bool redo = false;
+  if constexpr (!kFixup) {
+    if (lane == 0) vote[wave] = dirty ? 1 : 0;
+    __syncthreads();
+    redo = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+  }
 
   // ---- epilogue: O / l, bf16 round-to-nearest-even, LSE ----
   if (!wave_valid) return;
@@ -674,6 +772,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_w64_kernel(AttnParams p)
           (m_run[h] + __log2f(l)) * 0.69314718055994531f + p.lse_offset;
     }
   }
+  // a marked workgroup: a NaN in dim 0 of its first row (wave 0, half 0, row 0,
+  // always valid), which the fix-up launch reads
+  if (!kFixup && redo && wave == 0 && lane == 0)
+    *(static_cast<bf16_bits*>(p.o) + bh * p.q_head_stride + qrow[0] * D) = (bf16_bits)0x7fc0u;
 #undef ISA_WAIT_ALL_BUT_LAST_TILE
 #undef ISA_BARRIER
 }
@@ -693,17 +795,25 @@ hipError_t launch_attention_w64(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(((total + 7) / 8) * 8));
   // whole tiles only when both segments are whole numbers of blocks
   const bool partial = p.grid.src_tail() != 0 || p.grid.ctx_tail() != 0;
+  // then the fix-up launch (a workgroup reads one value and exits unless the
+  // first launch marked it)
+#define ISA_W64_LAUNCH(S, PART)                                                            \
+  hipLaunchKernelGGL((attn_fwd_w64_kernel<S, PART, false>), grid, dim3(kThreads), 0, stream, p); \
+  hipLaunchKernelGGL((attn_fwd_w64_kernel<S, PART, true>), grid, dim3(kThreads), 0, stream, p);
   if (p.half_shift == 1) {
-    if (partial)
-      hipLaunchKernelGGL((attn_fwd_w64_kernel<1, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_w64_kernel<1, false>), grid, dim3(kThreads), 0, stream, p);
+    if (partial) {
+      ISA_W64_LAUNCH(1, true)
+    } else {
+      ISA_W64_LAUNCH(1, false)
+    }
   } else {
-    if (partial)
-      hipLaunchKernelGGL((attn_fwd_w64_kernel<2, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_w64_kernel<2, false>), grid, dim3(kThreads), 0, stream, p);
+    if (partial) {
+      ISA_W64_LAUNCH(2, true)
+    } else {
+      ISA_W64_LAUNCH(2, false)
+    }
   }
+#undef ISA_W64_LAUNCH
   return hipGetLastError();
 }
 

@@ -12,10 +12,12 @@ because the exact tiles of the block mask read their valid-token count from the
 block grid on both paths.
 
 The 4-wave kernel on block tables (ISA_DEBUG_4WAVE_EXACT): by default the
-exact path and the dense baseline run on the ping-pong kernel and the 4-wave
-kernel reads only pooled rows through a row table; with the switch it reads
-whole blocks through the block table instead.  Those cases are checked against
-the fp64 oracle, at every block length and with partial blocks.
+exact path and the dense baseline run on the one-wave-per-SIMD kernel (the
+ping-pong kernel at b = 32) and the 4-wave kernel reads only pooled rows
+through a row table; with the switch it reads whole blocks through the block
+table instead.  Those cases are checked against the fp64 oracle, at every
+block length and with partial blocks; so is the ping-pong kernel
+(ISA_DEBUG_PINGPONG_EXACT) beside the default one.
 
 Every case prints its name, shape and seed (flushed) before touching the GPU.
 """
@@ -115,38 +117,23 @@ def test_4wave_dense_matches_oracle(D):
     O_ref, L_ref = orc.dense_ref(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v")))
     mx, mn = check_close(out_f64(o4), O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (4-wave)")
     check_close(l4.cpu().numpy(), L_ref, 5e-3, 1e-3, "LSE (4-wave)")
-    # same keys in the same tile order and the same per-row arithmetic as the
-    # ping-pong kernel: identical bits
-    assert torch.equal(o4, od) and torch.equal(l4, ld)
-    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}; equal to the ping-pong kernel")
+    # the default kernel (one wave per SIMD) on the same input, also against the
+    # oracle: the two take their exponentials against different references
+    # (the running row max, the first tile's row max), so their bits differ
+    check_close(out_f64(od), O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (default)")
+    check_close(ld.cpu().numpy(), L_ref, 5e-3, 1e-3, "LSE (default)")
+    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}")
 
 
 # The one-wave-per-SIMD kernel (the default for block tables at D = 128 with
-# 64- and 128-token blocks) against the 8-wave ping-pong kernel
-# (ISA_DEBUG_PINGPONG_EXACT): the same keys in the same tile order, the same
-# per-row exponentials, running-max updates and row sums, and the same product
-# order into O, so the two must agree bit for bit.  The cases cover one to
-# five key tiles (the three-tile prefetch ring and the tiles past the end),
-# odd and even tile counts (the loop body runs two tiles per trip), both block
-# lengths, and partial tiles.
-def _isa_both(inp, L_src, L_ctx, b, a_s, a_f):
-    def run():
-        plan = isa.isa_plan_create(1, 2, L_src, L_ctx, 128, b, a_s, a_f, dtype=torch.bfloat16)
-        q, k, v = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v"))
-        o, lse, aux = isa.isa_forward(plan, q, k, v, aux=True)
-        torch.cuda.synchronize()
-        return o, lse, aux
-    o1, l1, a1 = run()
-    isa.isa_debug_set_flags(isa.ISA_DEBUG_PINGPONG_EXACT)
-    try:
-        o2, l2, a2 = run()
-    finally:
-        isa.isa_debug_set_flags(0)
-    for key in a1:
-        assert torch.equal(a1[key], a2[key]), key
-    return (o1, l1), (o2, l2)
-
-
+# 64- and 128-token blocks) and the 8-wave ping-pong kernel
+# (ISA_DEBUG_PINGPONG_EXACT) on the same keys in the same tile order, each
+# against the oracle.  (The ping-pong kernel takes each tile's exponentials
+# against the running row max; the one-wave kernel against the first tile's
+# row max, raised only when a tile's row sum exceeds 2^8: their bits differ.)
+# The cases cover one to twenty-one key tiles (the three-tile prefetch ring and
+# the tiles past the end), odd and even tile counts (the loop body runs two
+# tiles per trip), both block lengths, and partial and empty half tiles.
 @pytest.mark.parametrize("b,L_src,L_ctx,a_s,a_f,seed", [
     (64, 1024, 1024, 0.25, 0.5, 321),    # aligned, 20 key tiles
     (64, 1088, 960, 0.25, 0.5, 322),     # aligned, 21 key tiles (odd)
@@ -157,19 +144,22 @@ def _isa_both(inp, L_src, L_ctx, b, a_s, a_f):
     (64, 128, 64, 0.0, 0.0, 327),        # two key tiles, nothing kept
     (64, 64, 0, 0.0, 0.0, 328),          # one key tile
 ])
-def test_w64_exact_path_equals_pingpong(b, L_src, L_ctx, a_s, a_f, seed):
-    _say(f"w64 vs ping-pong B1 H2 L_src{L_src} L_ctx{L_ctx} D128 b{b} as{a_s} af{a_f} seed{seed}")
+def test_w64_and_pingpong_exact_paths_match_oracle(b, L_src, L_ctx, a_s, a_f, seed):
+    _say(f"w64 and ping-pong B1 H2 L_src{L_src} L_ctx{L_ctx} D128 b{b} as{a_s} af{a_f} seed{seed}")
     inp = generate(1, 2, L_src, L_ctx, 128, b, seed=seed, variant="icl")
-    (o1, l1), (o2, l2) = _isa_both(inp, L_src, L_ctx, b, a_s, a_f)
-    assert torch.equal(o1, o2)
-    assert torch.equal(l1, l2)
-    _say("ok bit-identical")
+    _block_parity(inp, "bf16", 1, 2, L_src, L_ctx, 128, b, a_s, a_f)
+    isa.isa_debug_set_flags(isa.ISA_DEBUG_PINGPONG_EXACT)
+    try:
+        _block_parity(inp, "bf16", 1, 2, L_src, L_ctx, 128, b, a_s, a_f)
+    finally:
+        isa.isa_debug_set_flags(0)
+    _say("ok both kernels")
 
 
 @pytest.mark.parametrize("N", [64, 128, 192, 320, 2048])
-def test_w64_dense_equals_pingpong_and_oracle(N):
+def test_w64_and_pingpong_dense_match_oracle(N):
     seed = 330 + N // 64
-    _say(f"w64 dense bf16 B1 H2 N{N} D128 seed{seed}")
+    _say(f"w64 and ping-pong dense bf16 B1 H2 N{N} D128 seed{seed}")
     inp = generate(1, 2, N, 0, 128, 64, seed=seed, variant="plain")
     q, k, v = (to_gpu(inp[x], "bf16") for x in ("q", "k", "v"))
     o1, l1 = isa.isa_dense_forward(q, k, v)
@@ -182,5 +172,6 @@ def test_w64_dense_equals_pingpong_and_oracle(N):
     O_ref, L_ref = orc.dense_ref(*(to_f64(inp[x], "bf16") for x in ("q", "k", "v")))
     mx, mn = check_close(out_f64(o1), O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (w64 dense)")
     check_close(l1.cpu().numpy(), L_ref, 5e-3, 1e-3, "LSE (w64 dense)")
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}; equal to the ping-pong kernel")
+    check_close(out_f64(o2), O_ref, BF16_MAX_ABS, BF16_MEAN_ABS, "O (ping-pong dense)")
+    check_close(l2.cpu().numpy(), L_ref, 5e-3, 1e-3, "LSE (ping-pong dense)")
+    _say(f"ok max-abs {mx:.2e} mean-abs {mn:.2e}")
