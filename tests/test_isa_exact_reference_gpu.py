@@ -3,14 +3,15 @@
 The kernel exponentiates each key tile against a running reference (the row
 maxima of the first tile) instead of the tile's own maxima, and checks the
 row sums of a tile before any product reads its exponentials: a sum above
-2^16 raises the reference (O and l are rescaled), one that overflowed sends
-the workgroup through a second pass from the exact row maxima.  These inputs
+2^8 raises the reference (O and l are rescaled by a power of two), one above
+2^64 marks the workgroup for a second launch that recomputes it from the
+exact row maxima over every tile.  These inputs
 make a late key block score far above the first tile, so that both rare paths
 run, and compare the result with the fp64 oracle:
   scale 10:  the block's scores exceed the first tile's by about 30 log2 units
              (row sums near 2^30: a rebase);
   scale 60:  by well over 128 log2 units (the exponentials overflow: the
-             second pass).
+             fix-up launch).
 The same inputs go through the dense call (identity key table, whole tiles),
 through ISA with every block kept and exact on partial blocks (the kernel's
 partial-tile variant) and at b = 128 (two tiles per block).
