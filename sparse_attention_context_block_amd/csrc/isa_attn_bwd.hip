@@ -145,6 +145,7 @@ __device__ inline int64_t xcd_lid(int n_per_head, int BH, bool* valid) {
 //                    doubles the cost of the operand reads.
 // --------------------------------------------------------------------------
 constexpr int kT16 = 512;
+constexpr int kPipe = 3;  // LDS operand reads run this many product steps ahead
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 template <int D>
@@ -223,6 +224,27 @@ struct Stager16 {
 __device__ __forceinline__ bf16x8_t ts_operand(const unsigned char* tr, int row0, int c, int q,
                                                int g) {
   return *reinterpret_cast<const bf16x8_t*>(tr + TS::off(row0 + q, (32 * c + 8 * g) * 2));
+}
+
+// A scheduling fence: the compiler moves no instruction across it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Runs NS steps whose operands come from LDS: step s reads its operands
+// (rd(s)) P steps before its products run (mm(s)), into a ring of P + 1
+// register slots the callers index with s % (P + 1).  Fenced, so the
+// compiler neither sinks the reads next to their use (one LDS latency per
+// product, the order it picks under register pressure) nor hoists them all.
+template <int NS, int P, typename Rd, typename Mm>
+__device__ __forceinline__ void pipelined(Rd rd, Mm mm) {
+#pragma unroll
+  for (int st = 0; st < P; ++st) rd(st);
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (st + P < NS) rd(st + P);
+    fence();
+    mm(st);
+    fence();
+  }
 }
 
 __device__ __forceinline__ bf16x8_t pack_slots(const f32x4_t& a, const f32x4_t& b) {
@@ -430,17 +452,30 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
           s[n][i] = 0.0f;
           dp[n][i] = 0.0f;
         }
+      // step st = 4 kk + n: the Q and dO operands of subtile n, chunk kk
+      constexpr int P = kPipe;
+      bf16x8_t ra[P + 1], rb[P + 1];
+      pipelined<4 * NKK, P>(
+          [&](int st) __attribute__((always_inline)) {
+            const int off = RS<D>::off(16 * (st & 3) + q, (32 * (st >> 2) + 8 * g) * 2);
+            ra[st % (P + 1)] = *reinterpret_cast<const bf16x8_t*>(qt + off);
+            rb[st % (P + 1)] = *reinterpret_cast<const bf16x8_t*>(ot + off);
+          },
+          [&](int st) __attribute__((always_inline)) {
+            const int n = st & 3, kk = st >> 2;
+            s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[st % (P + 1)], kreg[kk], s[n], 0,
+                                                            0, 0);
+            dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[st % (P + 1)], vreg[kk], dp[n],
+                                                             0, 0, 0);
+          });
+      // step st = 2 j + c of the dV, dK products: the dO^T and Q^T operands of
+      // dims 16 j .. + 15, query chunk c; the first reads overlap the softmax
+      auto rd_t = [&](int st) __attribute__((always_inline)) {
+        ra[st % (P + 1)] = ts_operand(otr, 16 * (st >> 1), st & 1, q, g);
+        rb[st % (P + 1)] = ts_operand(qtr, 16 * (st >> 1), st & 1, q, g);
+      };
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {  // eight independent accumulator chains
-          const int off = RS<D>::off(16 * n + q, (32 * kk + 8 * g) * 2);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qt + off);
-          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[kk], s[n], 0, 0, 0);
-          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(ot + off);
-          dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, vreg[kk], dp[n], 0, 0, 0);
-        }
-      }
+      for (int st = 0; st < P; ++st) rd_t(st);
       // P and dS; the query chunk c of the B operands takes subtiles 2c, 2c + 1
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -456,19 +491,17 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dkdv16_kernel(BwdParams p) {
           dp[n][i] = pr * (dp[n][i] - dv4[i]);
         }
       }
-      const bf16x8_t pk0 = pack_slots(s[0], s[1]), pk1 = pack_slots(s[2], s[3]);
-      const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
+      const bf16x8_t pk[2] = {pack_slots(s[0], s[1]), pack_slots(s[2], s[3])};
+      const bf16x8_t ds[2] = {pack_slots(dp[0], dp[1]), pack_slots(dp[2], dp[3])};
       // dV^T += dO^T P, dK^T += Q^T dS: dims 16 j + 4 g + i of key q
 #pragma unroll
-      for (int j = 0; j < ND; ++j) {
-        const bf16x8_t a0 = ts_operand(otr, 16 * j, 0, q, g);
-        dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, pk0, dv[j], 0, 0, 0);
-        const bf16x8_t b0 = ts_operand(qtr, 16 * j, 0, q, g);
-        dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, ds0, dk[j], 0, 0, 0);
-        const bf16x8_t a1 = ts_operand(otr, 16 * j, 1, q, g);
-        dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pk1, dv[j], 0, 0, 0);
-        const bf16x8_t b1 = ts_operand(qtr, 16 * j, 1, q, g);
-        dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, ds1, dk[j], 0, 0, 0);
+      for (int st = 0; st < 2 * ND; ++st) {
+        if (st + P < 2 * ND) rd_t(st + P);
+        fence();
+        const int j = st >> 1, c = st & 1;
+        dv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[st % (P + 1)], pk[c], dv[j], 0, 0, 0);
+        dk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[st % (P + 1)], ds[c], dk[j], 0, 0, 0);
+        fence();
       }
     }
     if (e + 1 < n_q) store(x, buf ^ 1);
@@ -731,17 +764,31 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
           s[n][i] = 0.0f;
           dp[n][i] = 0.0f;
         }
+      // step st = 4 kk + n: the K and V operands of subtile n, chunk kk
+      constexpr int P = kPipe;
+      bf16x8_t ra[P + 1], rb[P + 1];
+      pipelined<4 * NKK, P>(
+          [&](int st) __attribute__((always_inline)) {
+            const int off = RS<D>::off(16 * (st & 3) + q, (32 * (st >> 2) + 8 * g) * 2);
+            ra[st % (P + 1)] = *reinterpret_cast<const bf16x8_t*>(kt + off);
+            rb[st % (P + 1)] = *reinterpret_cast<const bf16x8_t*>(vt + off);
+          },
+          [&](int st) __attribute__((always_inline)) {
+            const int n = st & 3, kk = st >> 2;
+            s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[st % (P + 1)], qreg[kk], s[n], 0,
+                                                            0, 0);
+            dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[st % (P + 1)], oreg[kk], dp[n],
+                                                             0, 0, 0);
+          });
+      // step st = 2 j + c of the dQ products (K^T operand of dims 16 j .. + 15,
+      // key chunk c), read 2 P steps ahead; the first reads overlap the softmax
+      constexpr int P2 = 2 * kPipe;
+      bf16x8_t rt[P2 + 1];
+      auto rd_t = [&](int st) __attribute__((always_inline)) {
+        rt[st % (P2 + 1)] = ts_operand(ktr, 16 * (st >> 1), st & 1, q, g);
+      };
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int off = RS<D>::off(16 * n + q, (32 * kk + 8 * g) * 2);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + off);
-          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s[n], 0, 0, 0);
-          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(vt + off);
-          dp[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, oreg[kk], dp[n], 0, 0, 0);
-        }
-      }
+      for (int st = 0; st < P2; ++st) rd_t(st);
       // keys past the end (only a row-table tile can be partial, or, with
       // general blocks, any tile past its slices' counts): P = 0
       const int valid = tok ? kBN : p.kv_rows - t * kBN;
@@ -769,14 +816,15 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
           dp[n][i] = live ? pr * (dp[n][i] - dlt) : 0.0f;
         }
       }
-      const bf16x8_t ds0 = pack_slots(dp[0], dp[1]), ds1 = pack_slots(dp[2], dp[3]);
+      const bf16x8_t ds[2] = {pack_slots(dp[0], dp[1]), pack_slots(dp[2], dp[3])};
       // dQ^T += K^T dS^T: dims 16 j + 4 g + i of query q
 #pragma unroll
-      for (int j = 0; j < ND; ++j) {
-        const bf16x8_t a0 = ts_operand(ktr, 16 * j, 0, q, g);
-        dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ds0, dq[j], 0, 0, 0);
-        const bf16x8_t a1 = ts_operand(ktr, 16 * j, 1, q, g);
-        dq[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ds1, dq[j], 0, 0, 0);
+      for (int st = 0; st < 2 * ND; ++st) {
+        if (st + P2 < 2 * ND) rd_t(st + P2);
+        fence();
+        dq[st >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rt[st % (P2 + 1)], ds[st & 1],
+                                                              dq[st >> 1], 0, 0, 0);
+        fence();
       }
     }
     if (t + 1 < n_tiles) store(x, buf ^ 1);
