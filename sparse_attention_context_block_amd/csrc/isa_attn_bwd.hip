@@ -145,7 +145,7 @@ __device__ inline int64_t xcd_lid(int n_per_head, int BH, bool* valid) {
 //                    doubles the cost of the operand reads.
 // --------------------------------------------------------------------------
 constexpr int kT16 = 512;
-constexpr int kPipe = 3;  // LDS operand reads run this many product steps ahead
+constexpr int kPipe = 2;  // LDS operand reads run this many product steps ahead
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 template <int D>
