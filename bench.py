@@ -784,6 +784,7 @@ def main():
     dense_equiv = 4.0 * B * H * N * N * D
     exact_flops = 4.0 * B * H * info["n_sharp"] * b * info["l_new"] * D
     taylor_flops = 4.0 * B * H * info["n_flat"] * b * info["n_kv_blocks"] * D
+    taylor_bytes = 2.0 * B * H * info["n_flat"] * b * D * 2 + 2.0 * B * H * info["n_kv_blocks"] * D * 2
     pool_bytes = 3.0 * B * H * N * D * 2 + B * H * info["n_q_blocks"] * D * (8 + 8 + 2 + 2)
     ex_ms = stage_ms["attn_exact"]
     achieved = exact_flops / (ex_ms * 1e-3) / 1e12
@@ -814,10 +815,15 @@ def main():
                                     2.0 * D * B * H * info["n_src_blocks"] * info["n_ctx_blocks"]),
         "select_route": {"ms": stage_ms["select_route"]},
         "attn_exact": {"ms": ex_ms, "TFLOP/s": achieved, "mfma_frac": achieved / PEAK_BF16_TFLOPS},
+        # the Taylor path sits near the bf16 ridge: its flops and its bytes (Q
+        # and O of the flat rows, the kept pooled rows once) against both roofs
         "attn_taylor": {"ms": stage_ms["attn_taylor"],
                         "TFLOP/s": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12,
                         "mfma_frac": taylor_flops / (stage_ms["attn_taylor"] * 1e-3) / 1e12
-                        / PEAK_BF16_TFLOPS},
+                        / PEAK_BF16_TFLOPS,
+                        "algorithmic_bytes": taylor_bytes,
+                        "hbm_frac": taylor_bytes / (stage_ms["attn_taylor"] * 1e-3) / 1e9
+                        / PEAK_HBM_GBS},
     }
     backward = None
     if args.bwd_workload != "none":

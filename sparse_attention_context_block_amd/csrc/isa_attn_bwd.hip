@@ -852,20 +852,22 @@ __global__ __launch_bounds__(kT16) void attn_bwd_dq16_kernel(BwdParams p) {
   }
 }
 
-// delta_r = dO_r . O_r over D (one thread per row, fp32)
+// delta_r = dO_r . O_r over D, fp32: D / 8 consecutive lanes per row, each
+// with one 16-byte load of O and of dO (a wave reads whole rows, so every load
+// instruction covers contiguous memory); the lanes' partial sums are combined
+// by a butterfly in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16_bits* __restrict__ O,
                                                              const bf16_bits* __restrict__ dO,
                                                              int64_t rows,
                                                              float* __restrict__ delta) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= rows) return;
-  const uint4* o = reinterpret_cast<const uint4*>(O + r * D);
-  const uint4* g = reinterpret_cast<const uint4*>(dO + r * D);
+  constexpr int kLanes = D / 8;  // 16 or 8 lanes per row
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t r = i / kLanes;
   float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    const uint4 a = o[i], b = g[i];
+  if (r < rows) {
+    const uint4 a = reinterpret_cast<const uint4*>(O)[i];
+    const uint4 b = reinterpret_cast<const uint4*>(dO)[i];
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -873,7 +875,10 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16_bits* __
       acc = fmaf(__uint_as_float(wa[k] & 0xffff0000u), __uint_as_float(wb[k] & 0xffff0000u), acc);
     }
   }
-  delta[r] = acc;
+  // (every lane of the wave takes part: rows never straddle a wave)
+#pragma unroll
+  for (int m = kLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (r < rows && (threadIdx.x & (kLanes - 1)) == 0) delta[r] = acc;
 }
 
 // Per (kept block t, head): block table entry and the bf16 means of the block's
@@ -1068,12 +1073,14 @@ hipError_t launch_backward(const BwdLaunch& L, hipStream_t s) {
 #define ISA_CHECK(x) \
   if ((e = (x)) != hipSuccess) return e;
   if (rows > 0) {
+    const int64_t threads = rows * (D / 8);
+    const dim3 dgrid((unsigned)((threads + kThreads - 1) / kThreads));
     if (D == 128)
-      hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3((unsigned)((rows + kThreads - 1) / kThreads)),
-                         dim3(kThreads), 0, s, L.O, L.dO, rows, L.delta);
+      hipLaunchKernelGGL(bwd_delta_kernel<128>, dgrid, dim3(kThreads), 0, s, L.O, L.dO, rows,
+                         L.delta);
     else
-      hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3((unsigned)((rows + kThreads - 1) / kThreads)),
-                         dim3(kThreads), 0, s, L.O, L.dO, rows, L.delta);
+      hipLaunchKernelGGL(bwd_delta_kernel<64>, dgrid, dim3(kThreads), 0, s, L.O, L.dO, rows,
+                         L.delta);
     ISA_CHECK(hipGetLastError());
   }
   BlockGrid grid;
