@@ -866,8 +866,8 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16_bits* __
   const int64_t r = i / kLanes;
   float acc = 0.0f;
   if (r < rows) {
-    const uint4 a = reinterpret_cast<const uint4*>(O)[i];
-    const uint4 b = reinterpret_cast<const uint4*>(dO)[i];
+    const uint4 a = load_nt(reinterpret_cast<const uint4*>(O) + i);
+    const uint4 b = load_nt(reinterpret_cast<const uint4*>(dO) + i);
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -897,21 +897,38 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     kv_tab[bh * n_kv + t] = blk;
     if (bh == 0) iota[t] = t;  // identity row table of the compact pooled rows
   }
-  __shared__ double red[2][kThreads / D * 2][D];
+  // D / 8 lanes per row, each summing one 16-byte chunk (8 dims) of every
+  // G-th row; the G row groups are then added in a fixed order.  (A sum of at
+  // most 128 bf16 values, 8 significant bits each, is exact in fp64 unless
+  // they span more than 2^38 in magnitude, so the order does not change it.)
+  constexpr int C = D / 8;         // 16-byte chunks per row
+  constexpr int G = kThreads / C;  // row groups
+  __shared__ double red[2][G][D];
   const int tid = threadIdx.x;
-  const int d = tid % D;
-  const int g = tid / D;           // row group
-  constexpr int G = kThreads / D;  // row groups
+  const int c = tid % C;
+  const int g = tid / C;
   const int rows = grid.rows(blk);
-  const bf16_bits* kb = K + (bh * grid.N + grid.start(blk)) * D;
-  const bf16_bits* vb = V + (bh * grid.N + grid.start(blk)) * D;
-  double sk = 0.0, sv = 0.0;
+  const bf16_bits* kb = K + (bh * grid.N + grid.start(blk)) * D + 8 * c;
+  const bf16_bits* vb = V + (bh * grid.N + grid.start(blk)) * D + 8 * c;
+  double sk[8], sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.0;
   for (int r = g; r < rows; r += G) {
-    sk += (double)__uint_as_float((uint32_t)kb[r * D + d] << 16);
-    sv += (double)__uint_as_float((uint32_t)vb[r * D + d] << 16);
+    const uint4 a = load_nt(kb + (int64_t)r * D), b = load_nt(vb + (int64_t)r * D);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sk[2 * w] += (double)__uint_as_float(wa[w] << 16);
+      sk[2 * w + 1] += (double)__uint_as_float(wa[w] & 0xffff0000u);
+      sv[2 * w] += (double)__uint_as_float(wb[w] << 16);
+      sv[2 * w + 1] += (double)__uint_as_float(wb[w] & 0xffff0000u);
+    }
   }
-  red[0][g][d] = sk;
-  red[1][g][d] = sv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red[0][g][8 * c + e] = sk[e];
+    red[1][g][8 * c + e] = sv[e];
+  }
   __syncthreads();
   if (tid < D) {
     double a = 0.0, b = 0.0;

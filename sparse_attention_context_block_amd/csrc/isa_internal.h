@@ -31,6 +31,15 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(double x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// 16 bytes at p with the nontemporal hint, for inputs a kernel reads once:
+// they stream through the caches instead of displacing what is reused (a plain
+// 1 GB read measured 6.3 against 5.1 TB/s when part of it was cache-resident).
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v x = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 // Height of the attention kernels' key and query tiles, and the block length
 // of the kernels that are built for one (the block-mask kernel, the backward).
 constexpr int kBlock = 64;

@@ -80,6 +80,7 @@ constexpr int kRopeHeads = 8;  // heads per workgroup when the kernel also rotat
 // kMode: 0 no rotation; 1 rotation with the angles of a block (of at most
 // kBlock rows) computed once for a group of kRopeHeads heads; 2 rotation with
 // the angles computed per row and head (longer blocks).
+
 template <typename T, int D, int kMode>
 __global__ __launch_bounds__(kThreads) void pool_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int BH, int N,
@@ -172,11 +173,13 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[2][e] += x[e];
     };
+    // every input row is read once here: nontemporal loads (0.200 -> 0.174 ms
+    // with warm caches, 0.251 -> 0.196 ms cold at the 32K shape, same box)
     auto load = [&](int r, uint4& uq, uint4& uk, uint4& uv) __attribute__((always_inline)) {
       const int64_t off = base + (int64_t)r * D;
-      uq = *reinterpret_cast<const uint4*>(Q + off);
-      uk = *reinterpret_cast<const uint4*>(K + off);
-      uv = *reinterpret_cast<const uint4*>(V + off);
+      uq = load_nt(Q + off);
+      uk = load_nt(K + off);
+      uv = load_nt(V + off);
     };
     if constexpr (kCache) {
       // the launcher guarantees block <= kBlock, so JMAX passes cover a block;
