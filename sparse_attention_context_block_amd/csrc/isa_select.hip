@@ -8,8 +8,10 @@
 //
 // Both are exact rank selections: every element's rank under the strict total
 // order (key, index) is counted against all others in LDS (n <= 4096 per
-// head, so O(n^2) comparisons spread over 256 threads is a few microseconds),
-// and the element is kept iff its rank is below the count.  The fp64 values are
+// head, so O(n^2) comparisons spread over 1024 threads; an element's count is
+// split over several adjacent lanes while there are fewer elements than
+// threads, and their integer parts are summed), and the element is kept iff its
+// rank is below the count.  The fp64 values are
 // compared through an order-preserving 64-bit integer key, so the order is
 // total even for NaN and exactly k (n_flat) elements are kept.  Lists are then
 // compacted in ascending index order with a fixed-order block scan.
@@ -23,6 +25,7 @@ namespace isa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSelThreads = 1024;  // select_route_kernel
 typedef double f64x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline uint64_t order_key(double x) {
@@ -37,7 +40,7 @@ __device__ inline uint64_t order_key(double x) {
 __device__ void compact(const uint8_t* flag, int n, int32_t* ones, int32_t* zeros,
                         int32_t* counts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + kThreads - 1) / kThreads;
+  const int per = (n + kSelThreads - 1) / kSelThreads;
   const int b = min(tid * per, n), e = min(b + per, n);
   int c = 0;
   for (int i = b; i < e; ++i) c += flag[i] ? 1 : 0;
@@ -61,49 +64,67 @@ __device__ void compact(const uint8_t* flag, int n, int32_t* ones, int32_t* zero
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void select_route_kernel(
+// flag[j] = 1 iff fewer than `keep` of the n keys precede key j in the strict
+// total order `before(key_i, i, key_j, j)`.  Element j's count is taken by P
+// adjacent lanes (P a power of two that divides the wave, all lanes of a
+// workgroup take the same number of rounds), lane `part` counting the keys
+// part, part + P, ...; a butterfly over the P lanes adds the parts.
+template <typename Before>
+__device__ void rank_flags(const uint64_t* key, int n, int keep, uint8_t* flag, Before before) {
+  int P = 1;
+  while (P < 64 && P * 2 * n <= kSelThreads) P *= 2;
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n * P; base += kSelThreads) {
+    const int x = base + tid, j = x / P, part = x % P;
+    int rank = 0;
+    if (j < n) {
+      const uint64_t kj = key[j];
+      int i = part;
+      for (; i + 7 * P < n; i += 8 * P) {  // eight LDS reads in flight
+        uint64_t kk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kk[u] = key[i + u * P];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += before(kk[u], i + u * P, kj, j) ? 1 : 0;
+      }
+      for (; i < n; i += P) rank += before(key[i], i, kj, j) ? 1 : 0;
+    }
+    for (int off = 1; off < P; off <<= 1) rank += __shfl_xor(rank, off, 64);
+    if (j < n && part == 0) flag[j] = rank < keep ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_route_kernel(
     const double* __restrict__ ctx_score, const double* __restrict__ sharpness, int n_src,
     int n_ctx, int n_q, int k, int n_flat, int32_t* __restrict__ sel, int32_t* __restrict__ flat,
     int32_t* __restrict__ sharp, int32_t* __restrict__ kv_tab) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* key = reinterpret_cast<uint64_t*>(smem);                // [n_q]
   uint8_t* flag = smem + sizeof(uint64_t) * kMaxBlocksPerHead;      // [n_q]
-  int32_t* counts = reinterpret_cast<int32_t*>(flag + kMaxBlocksPerHead);  // [kThreads]
+  int32_t* counts = reinterpret_cast<int32_t*>(flag + kMaxBlocksPerHead);  // [waves]
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   int32_t* sel_h = sel + bh * k;
   int32_t* tab_h = kv_tab + bh * (int64_t)(n_src + k);
 
   // ---- TopK over c_j (descending, ties to the smaller j) ----
-  for (int j = tid; j < n_ctx; j += kThreads) key[j] = order_key(ctx_score[bh * n_ctx + j]);
+  for (int j = tid; j < n_ctx; j += kSelThreads) key[j] = order_key(ctx_score[bh * n_ctx + j]);
   __syncthreads();
-  for (int j = tid; j < n_ctx; j += kThreads) {
-    const uint64_t kj = key[j];
-    int rank = 0;
-    for (int i = 0; i < n_ctx; ++i) {
-      const uint64_t ki = key[i];
-      rank += (ki > kj || (ki == kj && i < j)) ? 1 : 0;
-    }
-    flag[j] = rank < k ? 1 : 0;
-  }
+  rank_flags(key, n_ctx, k, flag, [](uint64_t ki, int i, uint64_t kj, int j) {
+    return ki > kj || (ki == kj && i < j);
+  });
   __syncthreads();
   compact(flag, n_ctx, sel_h, nullptr, counts);
-  for (int t = tid; t < n_src + k; t += kThreads)
+  for (int t = tid; t < n_src + k; t += kSelThreads)
     tab_h[t] = t < n_src ? t : n_src + sel_h[t - n_src];
   __syncthreads();
 
   // ---- routing over M_i (ascending, ties to the smaller i) ----
-  for (int i = tid; i < n_q; i += kThreads) key[i] = order_key(sharpness[bh * n_q + i]);
+  for (int i = tid; i < n_q; i += kSelThreads) key[i] = order_key(sharpness[bh * n_q + i]);
   __syncthreads();
-  for (int i = tid; i < n_q; i += kThreads) {
-    const uint64_t ki = key[i];
-    int rank = 0;
-    for (int j = 0; j < n_q; ++j) {
-      const uint64_t kj = key[j];
-      rank += (kj < ki || (kj == ki && j < i)) ? 1 : 0;
-    }
-    flag[i] = rank < n_flat ? 1 : 0;
-  }
+  rank_flags(key, n_q, n_flat, flag, [](uint64_t kj, int j, uint64_t ki, int i) {
+    return kj < ki || (kj == ki && j < i);
+  });
   __syncthreads();
   compact(flag, n_q, flat + bh * n_flat, sharp + bh * (int64_t)(n_q - n_flat), counts);
 }
@@ -337,8 +358,8 @@ hipError_t launch_select_route(const double* ctx_score, const double* sharpness,
                                hipStream_t stream) {
   if (BH == 0) return hipSuccess;
   const size_t lds = sizeof(uint64_t) * kMaxBlocksPerHead + kMaxBlocksPerHead +
-                     sizeof(int32_t) * kThreads;
-  hipLaunchKernelGGL(select_route_kernel, dim3(BH), dim3(kThreads), lds, stream, ctx_score,
+                     sizeof(int32_t) * (kSelThreads / 64);
+  hipLaunchKernelGGL(select_route_kernel, dim3(BH), dim3(kSelThreads), lds, stream, ctx_score,
                      sharpness, n_src, n_ctx, n_q, k, n_flat, sel, flat, sharp, kv_tab);
   return hipGetLastError();
 }
